@@ -1,0 +1,16 @@
+"""CPU float64 oracle (test infrastructure only; see ``fll_oracle``)."""
+
+from .fll_oracle import (  # noqa: F401
+    HEAD_KL,
+    HEAD_SELECTIVE,
+    dlogits,
+    fwd_bwd,
+    kl_rows,
+    log_softmax,
+    logits,
+    reduction_scale,
+    row_weights,
+    sampled_rows,
+    selective_rows,
+    valid_rows,
+)

@@ -1,0 +1,65 @@
+"""Write the golden regression fixtures from the CPU oracle.
+
+Run from the repository root: ``python tests/golden/make_golden.py``. It
+calls only ``oracle/`` (on inputs from ``workloads``) and stores the results
+as text, so that a later change to the oracle's arithmetic shows up as a
+failing ``test_golden.py`` and has to be justified.
+"""
+
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import workloads  # noqa: E402
+from oracle import fll_oracle  # noqa: E402
+
+CASES = {
+    # KL distillation, bf16 inputs, trainable head with bias, ignored rows.
+    "kl_bf16_small": workloads.small_case(
+        BT=12, H=16, V=40, dtype="bf16", head="kl", has_bias=True,
+        compute_dW=True, compute_db=True, temperature=2.0, ignore_frac=0.25,
+        seed=7),
+    # Selective log-prob, fp32 inputs, frozen head.
+    "selective_fp32_small": workloads.small_case(
+        BT=10, H=8, V=33, dtype="fp32", head="selective", reduction="mean",
+        x_std=1.0, w_std=0.5, seed=8),
+}
+
+
+def run_case(case):
+    inp = workloads.make_inputs(case)
+
+    def np_(t):
+        return None if t is None else t.double().numpy()
+
+    out = fll_oracle.fwd_bwd(
+        np_(inp["X"]), np_(inp["W"]), np_(inp["b"]), head=case.head,
+        labels=None if inp["labels"] is None else inp["labels"].numpy(),
+        target=np_(inp["target"]), weights=np_(inp["weights"]),
+        reduction=case.reduction, ignore_index=case.ignore_index,
+        temperature=case.temperature, eps=case.eps,
+        compute_dW=case.compute_dW, compute_db=case.compute_db)
+    rec = dict(loss=out["loss"], per_row=out["per_row"].tolist(),
+               n_valid=out["n_valid"], dX_row0=out["dX"][0].tolist(),
+               dX_sum=float(out["dX"].sum()))
+    if out["dW"] is not None:
+        rec["dW_row0"] = out["dW"][0].tolist()
+    if out["db"] is not None:
+        rec["db"] = out["db"].tolist()
+    return rec
+
+
+def main():
+    for name, case in CASES.items():
+        path = os.path.join(HERE, f"{name}.json")
+        with open(path, "w") as f:
+            json.dump(dict(case=case.name, source="oracle/fll_oracle.py fwd_bwd",
+                           values=run_case(case)), f, indent=1)
+        print("wrote", path)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+"""Planted mistakes in the oracle must fail its pins.
+
+Each mutation below replaces one oracle step (on the CPU, through
+monkeypatch) with a plausible slip. The test runs the pin tests of
+``test_oracle_pins`` against the mutated oracle and requires that at least
+one of them fails. This shows the pins are strong enough to catch the
+mistake, not only that the correct oracle passes them.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import fll_oracle as O
+from tests import test_oracle_pins as P
+
+_orig = {name: getattr(O, name) for name in
+         ("logits", "kl_rows", "selective_rows", "dlogits", "reduction_scale",
+          "valid_rows", "log_softmax")}
+
+
+def _kl_without_entropy(logP, target, valid, eps):
+    L = np.zeros(logP.shape[0])
+    r = np.nonzero(valid)[0]
+    L[r] = (-np.asarray(target, float)[r] * logP[r]).sum(axis=1)
+    return L
+
+
+def _kl_with_logits_not_logprobs(logP, target, valid, eps):
+    # uses S - max instead of S - lse
+    return _orig["kl_rows"](logP - logP.max(axis=1, keepdims=True), target, valid, eps)
+
+
+def _selective_negated(logP, labels, valid):
+    return -_orig["selective_rows"](logP, labels, valid)
+
+
+def _selective_off_by_one(logP, labels, valid):
+    y = (np.asarray(labels) + 1) % logP.shape[1]
+    y = np.where(np.asarray(labels) == -100, -100, y)
+    return _orig["selective_rows"](logP, y, valid)
+
+
+def _dlogits_no_tau(head, logP, target, labels, w, valid, g, temperature):
+    return _orig["dlogits"](head, logP, target, labels, w, valid, g, 1.0)
+
+
+def _dlogits_q_normalised(head, logP, target, labels, w, valid, g, temperature):
+    if head != "kl":
+        return _orig["dlogits"](head, logP, target, labels, w, valid, g, temperature)
+    dS = np.zeros_like(logP)
+    r = np.nonzero(valid)[0]
+    q = np.asarray(target, float)[r]
+    dS[r] = g * (np.exp(logP[r]) - q)  # assumes sum_v q = 1
+    return dS / temperature
+
+
+def _dlogits_wrong_sign(head, logP, target, labels, w, valid, g, temperature):
+    return -_orig["dlogits"](head, logP, target, labels, w, valid, g, temperature)
+
+
+def _scale_mean_ignores_V(head, reduction, n_valid, V):
+    return _orig["reduction_scale"]("selective", reduction, n_valid, V)
+
+
+def _scale_counts_ignored(head, reduction, n_valid, V):
+    return _orig["reduction_scale"](head, reduction, max(n_valid, 1) + 1, V)
+
+
+def _logits_drop_bias(X, W, b, temperature):
+    return _orig["logits"](X, W, None, temperature)
+
+
+def _logits_tau_multiplies(X, W, b, temperature):
+    return _orig["logits"](X, W, b, 1.0 / temperature)
+
+
+def _log_softmax_unshifted_lse(S):
+    logP, lse = _orig["log_softmax"](S)
+    return logP + 1e-3, lse
+
+
+def _valid_all_rows(labels, ignore_index, BT):
+    return np.ones(BT, dtype=bool)
+
+
+MUTATIONS = {
+    "kl drops sum q log q": ("kl_rows", _kl_without_entropy),
+    "kl uses S - max": ("kl_rows", _kl_with_logits_not_logprobs),
+    "selective negated": ("selective_rows", _selective_negated),
+    "selective label off by one": ("selective_rows", _selective_off_by_one),
+    "dZ misses 1/tau": ("dlogits", _dlogits_no_tau),
+    "KL grad assumes sum q = 1": ("dlogits", _dlogits_q_normalised),
+    "gradient sign flipped": ("dlogits", _dlogits_wrong_sign),
+    "KL mean ignores V": ("reduction_scale", _scale_mean_ignores_V),
+    "ignored rows counted": ("reduction_scale", _scale_counts_ignored),
+    "bias dropped": ("logits", _logits_drop_bias),
+    "tau multiplies": ("logits", _logits_tau_multiplies),
+    "log-softmax off by a constant": ("log_softmax", _log_softmax_unshifted_lse),
+    "ignore mask ignored": ("valid_rows", _valid_all_rows),
+}
+
+
+def _pin_tests():
+    tests = []
+    for name in dir(P):
+        if not name.startswith("test_"):
+            continue
+        fn = getattr(P, name)
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if not params:
+            tests.append((name, fn, {}))
+            continue
+        argnames, values = params[0].args[0], params[0].args[1]
+        names = [a.strip() for a in argnames.split(",")]
+        for v in values:
+            v = v if isinstance(v, tuple) else (v,)
+            if name == "test_gradients_central_differences" and v[2] != 2.0:
+                continue  # one temperature suffices here; keeps the run short
+            tests.append((f"{name}{v}", fn, dict(zip(names, v))))
+    return tests
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_pins_catch_mutation(mutation, monkeypatch):
+    attr, fn = MUTATIONS[mutation]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for name, test, kwargs in _pin_tests():
+        try:
+            test(**kwargs)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(name)
+    assert caught, f"no pin fails when the oracle has the slip: {mutation}"

@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks the oracle against what the pages and the mathematics fix:
+closed forms, invariants (Gibbs' inequality, zero row sums of the
+log-softmax backward), special cases that reduce to torch library routines
+evaluated in float64 (``log_softmax``, ``cross_entropy``, ``kl_div``,
+autograd), central finite differences and an exact temperature identity.
+They are chosen so that a plausible slip in the oracle -- a dropped term, a
+wrong sign, a wrong index, a transposed operand, a missing 1/tau, a wrong
+denominator -- fails at least one of them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import fll_oracle as O
+
+rng = np.random.default_rng(20261202)
+
+
+def _rand(*shape, std=1.0):
+    return rng.normal(0.0, std, size=shape)
+
+
+def _softmax(a):
+    e = np.exp(a - a.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# logits and log-softmax
+# --------------------------------------------------------------------------
+
+def test_logits_match_torch_linear():
+    X, W, b = _rand(7, 5), _rand(11, 5), _rand(11)
+    S = O.logits(X, W, b, 2.0)
+    ref = F.linear(torch.tensor(X), torch.tensor(W), torch.tensor(b)) / 2.0
+    np.testing.assert_allclose(S, ref.numpy(), rtol=1e-14, atol=1e-14)
+    assert S.shape == (7, 11)
+
+
+def test_log_softmax_closed_form_uniform():
+    # W = 0, b = 0: every logit is 0, so log p = -log V exactly.
+    for V in (1, 2, 7, 1000):
+        S = O.logits(_rand(3, 4), np.zeros((V, 4)), np.zeros(V), 1.0)
+        logP, lse = O.log_softmax(S)
+        np.testing.assert_allclose(logP, -math.log(V), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse, math.log(V), rtol=0, atol=1e-15)
+
+
+def test_log_softmax_two_class_closed_form():
+    # logits [0, log 3] -> p = [1/4, 3/4].
+    S = np.array([[0.0, math.log(3.0)]])
+    logP, _ = O.log_softmax(S)
+    np.testing.assert_allclose(logP[0], [math.log(0.25), math.log(0.75)], rtol=1e-15)
+
+
+def test_log_softmax_matches_torch_and_shift_invariance():
+    S = _rand(6, 50, std=5.0)
+    logP, _ = O.log_softmax(S)
+    np.testing.assert_allclose(logP, torch.log_softmax(torch.tensor(S), 1).numpy(),
+                               rtol=1e-13, atol=1e-13)
+    shifted, _ = O.log_softmax(S + _rand(6, 1, std=100.0))
+    np.testing.assert_allclose(shifted, logP, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.exp(logP).sum(1), 1.0, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# KL head
+# --------------------------------------------------------------------------
+
+def _kl_case(BT=9, H=6, V=13, tau=1.0, bias=True):
+    X, W = _rand(BT, H), _rand(V, H)
+    b = _rand(V) if bias else None
+    q = _softmax(_rand(BT, V, std=2.0))
+    return X, W, b, q
+
+
+def test_kl_two_class_closed_form():
+    # p = [1/4, 3/4], q = [1/2, 1/2]: KL = 1/2 log 2 + 1/2 log(2/3) = 1/2 log(4/3),
+    # dS = Q p - q = [-1/4, 1/4].
+    X = np.array([[1.0]])
+    W = np.array([[0.0], [math.log(3.0)]])
+    q = np.array([[0.5, 0.5]])
+    out = O.fwd_bwd(X, W, head="kl", target=q, reduction="sum")
+    assert out["loss"] == pytest.approx(0.5 * math.log(4.0 / 3.0), rel=1e-15)
+    # dX = dZ W = -1/4 * 0 + 1/4 * log 3
+    assert out["dX"][0, 0] == pytest.approx(0.25 * math.log(3.0), rel=1e-15)
+    np.testing.assert_allclose(out["db"], [-0.25, 0.25], rtol=1e-15)
+    np.testing.assert_allclose(out["dW"][:, 0], [-0.25, 0.25], rtol=1e-15)
+
+
+def test_kl_zero_when_target_is_model_softmax():
+    X, W, b, _ = _kl_case()
+    for tau in (0.5, 1.0, 2.0):
+        S = O.logits(X, W, b, tau)
+        q = _softmax(S)
+        out = O.fwd_bwd(X, W, b, head="kl", target=q, temperature=tau,
+                        reduction="sum")
+        # logits reach |S| ~ 20 here, so fp64 rounding leaves ~1e-12
+        assert abs(out["loss"]) < 1e-11
+        assert np.abs(out["dX"]).max() < 1e-13
+        assert np.abs(out["dW"]).max() < 1e-13
+        assert np.abs(out["db"]).max() < 1e-13
+
+
+def test_kl_nonnegative():
+    for seed in range(5):
+        X, W, b, q = _kl_case()
+        out = O.fwd_bwd(X, W, b, head="kl", target=q, reduction="sum")
+        assert (out["per_row"] >= -1e-14).all()
+        assert out["loss"] > 0
+
+
+@pytest.mark.parametrize("reduction", ["batchmean", "sum", "mean"])
+def test_kl_matches_torch_kl_div(reduction):
+    X, W, b, q = _kl_case(BT=12, V=17)
+    q[0, 3] = 0.0  # an exact zero: 0 * log 0 must contribute 0
+    q[0] /= q[0].sum()
+    for tau in (0.5, 2.0):
+        out = O.fwd_bwd(X, W, b, head="kl", target=q, temperature=tau,
+                        reduction=reduction)
+        logP = torch.log_softmax(torch.tensor(O.logits(X, W, b, tau)), 1)
+        ref = F.kl_div(logP, torch.tensor(q), reduction=reduction, log_target=False)
+        assert out["loss"] == pytest.approx(float(ref), rel=1e-12)
+
+
+def test_kl_ignored_rows_leave_the_batch():
+    X, W, b, q = _kl_case(BT=10, V=9)
+    labels = np.arange(10)
+    labels[[1, 4, 7]] = -100
+    q_nan = q.copy()
+    q_nan[[1, 4, 7]] = np.nan  # never read
+    out = O.fwd_bwd(X, W, b, head="kl", target=q_nan, labels=labels,
+                    reduction="batchmean")
+    keep = labels != -100
+    logP = torch.log_softmax(torch.tensor(O.logits(X[keep], W, b, 1.0)), 1)
+    ref = F.kl_div(logP, torch.tensor(q[keep]), reduction="batchmean")
+    assert out["n_valid"] == 7
+    assert out["loss"] == pytest.approx(float(ref), rel=1e-12)
+    assert np.isfinite(out["dX"]).all()
+    assert (out["dX"][~keep] == 0).all()
+    # moving ignored rows' inputs changes nothing
+    X2 = X.copy()
+    X2[~keep] += 10.0
+    out2 = O.fwd_bwd(X2, W, b, head="kl", target=q_nan, labels=labels)
+    assert out2["loss"] == out["loss"]
+    np.testing.assert_array_equal(out2["dX"][keep], out["dX"][keep])
+
+
+def test_kl_one_hot_target_is_cross_entropy():
+    X, W, b, _ = _kl_case(BT=8, V=11)
+    y = rng.integers(0, 11, size=8)
+    q = np.zeros((8, 11))
+    q[np.arange(8), y] = 1.0
+    out = O.fwd_bwd(X, W, b, head="kl", target=q, reduction="sum")
+    ce = F.cross_entropy(torch.tensor(O.logits(X, W, b, 1.0)), torch.tensor(y),
+                         reduction="none")
+    np.testing.assert_allclose(out["per_row"], ce.numpy(), rtol=1e-13)
+
+
+def test_kl_reduction_identities():
+    X, W, b, q = _kl_case(BT=6, V=10)
+    labels = np.array([0, -100, 2, 3, -100, 5])
+    o = {r: O.fwd_bwd(X, W, b, head="kl", target=q, labels=labels, reduction=r)
+         for r in ("batchmean", "mean", "sum")}
+    n, V = 4, 10
+    assert o["sum"]["loss"] == pytest.approx(n * o["batchmean"]["loss"], rel=1e-14)
+    assert o["sum"]["loss"] == pytest.approx(n * V * o["mean"]["loss"], rel=1e-14)
+    np.testing.assert_allclose(o["sum"]["dX"], n * o["batchmean"]["dX"], rtol=1e-13)
+
+
+def test_reduction_none_refused():
+    with pytest.raises(ValueError):
+        O.reduction_scale("kl", "none", 3, 5)
+
+
+def test_no_valid_rows_gives_zero():
+    X, W, b, q = _kl_case(BT=4, V=5)
+    labels = np.full(4, -100)
+    out = O.fwd_bwd(X, W, b, head="kl", target=np.full((4, 5), np.nan),
+                    labels=labels)
+    assert out["loss"] == 0.0 and out["n_valid"] == 0
+    assert (out["dX"] == 0).all() and (out["dW"] == 0).all() and (out["db"] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# selective head
+# --------------------------------------------------------------------------
+
+def test_selective_matches_negative_cross_entropy():
+    X, W, b = _rand(10, 6), _rand(15, 6), _rand(15)
+    y = rng.integers(0, 15, size=10)
+    y[3] = -100
+    out = O.fwd_bwd(X, W, b, head="selective", labels=y, reduction="mean")
+    ce = F.cross_entropy(torch.tensor(O.logits(X, W, b, 1.0)), torch.tensor(y),
+                         ignore_index=-100, reduction="mean")
+    assert out["loss"] == pytest.approx(-float(ce), rel=1e-13)
+
+
+def test_selective_weighted_matches_torch():
+    X, W = _rand(10, 6), _rand(15, 6)
+    y = rng.integers(0, 15, size=10)
+    w = _rand(10)
+    for tau in (0.5, 1.0):
+        out = O.fwd_bwd(X, W, head="selective", labels=y, weights=w,
+                        temperature=tau, reduction="mean")
+        ce = F.cross_entropy(torch.tensor(O.logits(X, W, None, tau)),
+                             torch.tensor(y), reduction="none")
+        ref = -(torch.tensor(w) * ce).sum() / 10
+        assert out["loss"] == pytest.approx(float(ref), rel=1e-13)
+        assert (out["per_row"] <= 0).all()
+
+
+def test_selective_uniform_logits_closed_form():
+    V = 37
+    X = _rand(8, 4)
+    y = rng.integers(0, V, size=8)
+    w = _rand(8)
+    out = O.fwd_bwd(X, np.zeros((V, 4)), np.zeros(V), head="selective",
+                    labels=y, weights=w, reduction="mean")
+    assert out["loss"] == pytest.approx(-math.log(V) * w.sum() / 8, rel=1e-14)
+
+
+def test_selective_label_out_of_range_raises():
+    with pytest.raises(ValueError):
+        O.fwd_bwd(_rand(2, 3), _rand(4, 3), head="selective", labels=np.array([0, 4]))
+
+
+# --------------------------------------------------------------------------
+# gradients
+# --------------------------------------------------------------------------
+
+def _loss_fn(kw):
+    def f(X, W, b):
+        return O.fwd_bwd(X, W, b, **kw)["loss"]
+    return f
+
+
+def _central_fd(f, args, i, h=1e-6):
+    base = [a.copy() if a is not None else None for a in args]
+    g = np.zeros_like(base[i])
+    it = np.nditer(base[i], flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        p = [a.copy() if a is not None else None for a in base]
+        m = [a.copy() if a is not None else None for a in base]
+        p[i][idx] += h
+        m[i][idx] -= h
+        g[idx] = (f(*p) - f(*m)) / (2 * h)
+    return g
+
+
+FD_CASES = []
+for head in ("kl", "selective"):
+    for reduction in ("batchmean", "mean", "sum"):
+        for tau in (0.5, 1.0, 2.0):
+            FD_CASES.append((head, reduction, tau))
+
+
+@pytest.mark.parametrize("head,reduction,tau", FD_CASES)
+def test_gradients_central_differences(head, reduction, tau):
+    BT, H, V = 5, 4, 7
+    X, W, b = _rand(BT, H), _rand(V, H), _rand(V)
+    labels = rng.integers(0, V, size=BT)
+    labels[2] = -100
+    kw = dict(head=head, labels=labels, reduction=reduction, temperature=tau)
+    if head == "kl":
+        q = _softmax(_rand(BT, V)) * 1.3  # unnormalised: exercises Q_r
+        kw["target"] = q
+    else:
+        kw["weights"] = _rand(BT)
+    out = O.fwd_bwd(X, W, b, **kw)
+    f = _loss_fn(kw)
+    for i, name in ((0, "dX"), (1, "dW"), (2, "db")):
+        fd = _central_fd(f, [X, W, b], i)
+        np.testing.assert_allclose(out[name], fd, rtol=1e-6, atol=1e-8,
+                                   err_msg=name)
+
+
+@pytest.mark.parametrize("head", ["kl", "selective"])
+def test_gradients_match_torch_autograd(head):
+    BT, H, V, tau = 33, 24, 57, 2.0
+    X, W, b = _rand(BT, H), _rand(V, H, std=0.3), _rand(V)
+    labels = rng.integers(0, V, size=BT)
+    labels[::7] = -100
+    keep = labels != -100
+    Xt, Wt, bt = (torch.tensor(a, requires_grad=True) for a in (X, W, b))
+    logP = torch.log_softmax(F.linear(Xt, Wt, bt) / tau, dim=1)
+    if head == "kl":
+        q = _softmax(_rand(BT, V, std=2.0))
+        loss_t = F.kl_div(logP[torch.tensor(keep)], torch.tensor(q[keep]),
+                          reduction="batchmean")
+        kw = dict(target=q, reduction="batchmean")
+    else:
+        w = _rand(BT)
+        ce = F.cross_entropy(F.linear(Xt, Wt, bt) / tau, torch.tensor(labels),
+                             ignore_index=-100, reduction="none")
+        loss_t = -(torch.tensor(w) * ce).sum() / keep.sum()
+        kw = dict(weights=w, reduction="mean")
+    loss_t.backward()
+    out = O.fwd_bwd(X, W, b, head=head, labels=labels, temperature=tau, **kw)
+    assert out["loss"] == pytest.approx(float(loss_t), rel=1e-12)
+    np.testing.assert_allclose(out["dX"], Xt.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(out["db"], bt.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("head", ["kl", "selective"])
+def test_dlogit_rows_sum_to_zero(head):
+    BT, V = 20, 300
+    logP, _ = O.log_softmax(_rand(BT, V, std=3.0))
+    labels = rng.integers(0, V, size=BT)
+    q = _softmax(_rand(BT, V)) * 0.7  # sum_v (Q p - q) = 0 for any scale
+    dZ = O.dlogits(head, logP, q, labels, _rand(BT), np.ones(BT, bool), 0.3, 2.0)
+    np.testing.assert_allclose(dZ.sum(axis=1), 0.0, atol=1e-15)
+
+
+@pytest.mark.parametrize("head", ["kl", "selective"])
+def test_temperature_power_of_two_identity(head):
+    # S = (X W^T + b)/tau equals X (W/tau)^T + b/tau exactly for tau = 2^k, so
+    # dX must agree bitwise, and dW(tau) = dW'(tau=1) / tau: pins where 1/tau
+    # enters the forward and the backward.
+    BT, H, V = 9, 8, 21
+    X, W, b = _rand(BT, H), _rand(V, H), _rand(V)
+    labels = rng.integers(0, V, size=BT)
+    kw = dict(head=head, labels=labels)
+    if head == "kl":
+        kw["target"] = _softmax(_rand(BT, V))
+    else:
+        kw["weights"] = _rand(BT)
+    for tau in (0.5, 2.0, 4.0):
+        a = O.fwd_bwd(X, W, b, temperature=tau, **kw)
+        c = O.fwd_bwd(X, W / tau, b / tau, temperature=1.0, **kw)
+        assert a["loss"] == c["loss"]
+        np.testing.assert_array_equal(a["dX"], c["dX"])
+        np.testing.assert_array_equal(a["dW"], c["dW"] / tau)
+        np.testing.assert_array_equal(a["db"], c["db"] / tau)
+
+
+def test_flags_do_not_change_dx():
+    X, W, b, q = _kl_case()
+    a = O.fwd_bwd(X, W, b, head="kl", target=q, compute_dW=False, compute_db=False)
+    c = O.fwd_bwd(X, W, b, head="kl", target=q, compute_dW=True, compute_db=True)
+    assert a["dW"] is None and a["db"] is None
+    np.testing.assert_array_equal(a["dX"], c["dX"])
+    assert a["loss"] == c["loss"]
+
+
+@pytest.mark.parametrize("head", ["kl", "selective"])
+def test_sampled_rows_agree_with_full(head):
+    BT, H, V = 16, 8, 29
+    X, W, b = _rand(BT, H), _rand(V, H), _rand(V)
+    labels = rng.integers(0, V, size=BT)
+    labels[[3, 9]] = -100
+    kw = dict(head=head, reduction="mean", temperature=2.0)
+    q = w = None
+    if head == "kl":
+        q = _softmax(_rand(BT, V))
+    else:
+        w = _rand(BT)
+    full = O.fwd_bwd(X, W, b, labels=labels, target=q, weights=w, **kw)
+    rows = np.array([0, 3, 5, 15])
+    sub = O.sampled_rows(X[rows], W, b, n_valid=full["n_valid"],
+                         labels_rows=labels[rows],
+                         target_rows=None if q is None else q[rows],
+                         weights_rows=None if w is None else w[rows], **kw)
+    np.testing.assert_array_equal(sub["per_row"], full["per_row"][rows])
+    np.testing.assert_allclose(sub["dX"], full["dX"][rows], rtol=1e-14, atol=1e-17)
