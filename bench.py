@@ -1,0 +1,207 @@
+"""Benchmark: fused lm_head loss, fwd+bwd tokens/s on one MI355X.
+
+A step is one ``fll_fwd_bwd`` call over the whole batch: every token chunk's
+logits GEMM, fused row kernel, dX GEMM (+ split reduction) and, for trainable
+heads, the dW / db kernels, then the loss reduction. Inputs are synthetic,
+seeded, and resident in HBM before timing starts.
+
+Default workload: GRPO selective log-prob with a frozen head, B=8, T=1024
+(BT = 8192 tokens), H = 4096, V = 128256, bf16 -- the head shape and batch
+the frozen lm_head GRPO page times (Details). ``--config 5`` selects the
+trainable KL distillation workload at the same H and V.
+
+Prints one JSON line. ``roofline`` covers the dominant kernel, timed with
+HIP events on the library's stream over the timed steps; ``cpu_baseline``
+times the CPU float64 oracle on a bounded row sample and extrapolates
+linearly in rows (every step of the method is row-local except the final
+sum).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd+bwd tokens/sec at H=4096,V=128256 bf16; % of bf16 MFMA peak"
+
+
+def gemm_flops(case):
+    """Algorithmic flops of one step: logits and dX GEMMs, plus dW if formed."""
+    f = 4.0 * case.BT * case.H * case.V
+    if case.compute_dW:
+        f += 2.0 * case.BT * case.H * case.V
+    return f
+
+
+def kernel_flops(kind, case):
+    per = 2.0 * case.BT * case.H * case.V
+    return {"logits": per, "dx": per, "dw": per if case.compute_dW else 0.0}.get(kind, 0.0)
+
+
+def cpu_baseline(inp, case, rows_small=32, rows_big=160):
+    """Time the oracle on two row samples and extrapolate to the full batch."""
+    import numpy as np
+
+    from oracle import fll_oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+
+    Wd = inp["W"]
+    bd = inp["b"]
+
+    def run(R):
+        rows = np.arange(R)
+        X = inp["X"][:R].double().numpy()
+        t0 = time.perf_counter()
+        fll_oracle.sampled_rows(
+            X, Wd.double().numpy(), None if bd is None else bd.double().numpy(),
+            head=case.head, n_valid=case.BT,
+            labels_rows=None if inp["labels"] is None else inp["labels"][rows].numpy(),
+            target_rows=None if inp["target"] is None else inp["target"][:R].double().numpy(),
+            weights_rows=None if inp["weights"] is None else inp["weights"][:R].double().numpy(),
+            reduction=case.reduction, ignore_index=case.ignore_index,
+            temperature=case.temperature, eps=case.eps)
+        return time.perf_counter() - t0
+
+    t1 = run(rows_small)
+    t2 = run(rows_big)
+    per_row = max((t2 - t1) / (rows_big - rows_small), 1e-12)
+    fixed = max(t1 - per_row * rows_small, 0.0)
+    est = fixed + per_row * case.BT
+    return {
+        "value": case.BT / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"numpy float64 oracle (sampled_rows: logits, log-softmax, loss terms, "
+                   f"dlogits, dX) timed on the first {rows_small} and {rows_big} token rows "
+                   f"({t1:.2f} s, {t2:.2f} s), extrapolated linearly to BT={case.BT}"
+                   + ("; the dW GEMM is not in the sample" if case.compute_dW else "")),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-rows", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the fused lm_head loss is a single-GPU "
+              "operator here; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lm_head_projection_token_amd as fll
+    import workloads
+
+    case = workloads.CONFIGS[args.config]
+    inp = workloads.make_inputs(case)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(t):
+        return None if t is None else t.to(dev).contiguous()
+
+    X, W, b = d(inp["X"]), d(inp["W"]), d(inp["b"])
+    labels, target, weights = d(inp["labels"]), d(inp["target"]), d(inp["weights"])
+    prob = fll.make_problem(case.BT, case.H, case.V, dtype=case.dtype, head=case.head,
+                            has_bias=case.has_bias, compute_dW=case.compute_dW,
+                            compute_db=case.compute_db, reduction=case.reduction,
+                            ignore_index=case.ignore_index, temperature=case.temperature,
+                            eps=case.eps)
+    plan = fll.fll_plan(prob, 0, args.chunk_rows)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    dX = torch.empty_like(X)
+    dW = torch.empty(case.V, case.H, dtype=torch.float32, device=dev) if case.compute_dW else None
+    db = torch.empty(case.V, dtype=torch.float32, device=dev) if case.compute_db else None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fll.fll_fwd_bwd(plan, X=X, W=W, b=b, labels=labels, target=target, weights=weights,
+                        dX=dX, dW=dW, db=db, loss=loss, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    fll.fll_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = fll.fll_profile_read(reset=True)
+    fll.fll_profile_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    if not torch.isfinite(loss):
+        raise RuntimeError("non-finite loss")
+
+    tokens_per_s = case.BT / (ms / 1e3)
+    peak = PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_FP32_TFLOPS
+    e2e_frac = gemm_flops(case) / (ms / 1e3) / 1e12 / peak
+
+    kernels = {}
+    for kind, (n, tot) in prof.items():
+        if n:
+            kernels[kind] = {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
+    gemms = [k for k in ("logits", "dx", "dw") if k in kernels]
+    dom = max(gemms, key=lambda k: kernels[k]["ms_per_step"])
+    per_launch = kernel_flops(dom, case) / plan.n_chunks
+    achieved = per_launch / (kernels[dom]["avg_ms"] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "flops_per_launch": per_launch}
+    row = kernels.get("row")
+    if row:
+        bytes_per_row = (10 if case.head == "kl" else 6) * case.V
+        n_valid = case.BT if inp["labels"] is None else int(
+            (inp["labels"] != case.ignore_index).sum())
+        row_bytes = bytes_per_row * n_valid / plan.n_chunks
+        kernels["row"]["achieved_GBps"] = row_bytes / (row["avg_ms"] / 1e3) / 1e9
+
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": case.name, "BT": case.BT, "H": case.H, "V": case.V,
+                   "head": case.head, "compute_dW": case.compute_dW,
+                   "compute_db": case.compute_db, "chunk_rows": plan.chunk_rows,
+                   "n_chunks": plan.n_chunks, "parallelism": "single GPU"},
+        "end_to_end_frac_of_bf16_peak": e2e_frac,
+        "wall_s": wall,
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, case)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,414 @@
+// Row-wise and reduction kernels of the fused lm_head loss (gfx950, wave64).
+//
+// The fused row kernel is the softmax / loss / dlogits step between the
+// logits GEMM and the gradient GEMMs: for one token row it forms the
+// log-sum-exp over the vocabulary, the row's loss term and the row's dlogits,
+// and writes the dlogits in place over the row's logits [FusedLinearKLDivLoss
+// page, Details: the log-softmax backward is computed in place on the saved
+// log-probs]. It streams the row from HBM with 16-byte coalesced loads; the
+// reductions run in registers, then across the wavefront with lane shuffles,
+// then across the four wavefronts of the workgroup through LDS.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "fll_internal.h"
+
+namespace fll {
+namespace {
+
+constexpr int kRowThreads = 256;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kUnroll = 4;  // float4 groups per thread per strip
+constexpr int kStrip = kRowThreads * kUnroll;  // float4 groups per strip
+
+constexpr int HEAD_KL = 0;
+constexpr int HEAD_SEL = 1;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Combine two (max, sum of exp(x - max)) pairs.
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+  float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  // round to nearest even; quiet NaN stays NaN
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+struct Load4 {
+  float v[4];
+};
+
+// Loads elements [4g, 4g + 4) of a row (clipped at V), 16-byte loads when the
+// group is whole and the row is 16-byte aligned.
+__device__ __forceinline__ Load4 load_group(const float *row, int64_t g, int64_t V,
+                                            bool vec_ok) {
+  Load4 r;
+  const int64_t e = 4 * g;
+  if (vec_ok && e + 4 <= V) {
+    float4 x = *reinterpret_cast<const float4 *>(row + e);
+    r.v[0] = x.x; r.v[1] = x.y; r.v[2] = x.z; r.v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = (e + i < V) ? row[e + i] : 0.0f;
+  }
+  return r;
+}
+
+template <int HEAD>
+__global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
+  __shared__ float red[kRowWaves][8];
+  __shared__ float bcast[8];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t lr = blockIdx.x;
+  const int64_t gr = a.row0 + lr;
+  const int64_t V = a.V;
+  float *Srow = a.S + lr * a.s_pitch;
+  unsigned short *Zb = reinterpret_cast<unsigned short *>(Srow);  // bf16 dZ
+  const int64_t ngroups = (V + 3) / 4;
+
+  int64_t y = 0;
+  bool valid = true;
+  if (a.labels) {
+    y = a.labels[gr];
+    valid = (y != a.ignore_index);
+  }
+  const bool bad_label = HEAD == HEAD_SEL && valid && (y < 0 || y >= V);
+  if (!valid || bad_label) {
+    // The row takes no part: its dlogits are zero.
+    for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+      const int64_t e = 4 * g;
+      for (int i = 0; i < 4; ++i) {
+        if (e + i < V) {
+          if (a.dz_bf16) Zb[e + i] = 0;
+          else Srow[e + i] = 0.0f;
+        }
+      }
+    }
+    if (tid == 0) a.rowval[gr] = bad_label ? NAN : 0.0f;
+    return;
+  }
+
+  const float *q = HEAD == HEAD_KL ? a.target + gr * V : nullptr;
+  const bool q_vec = HEAD == HEAD_KL && (V % 4 == 0) &&
+                     ((reinterpret_cast<uintptr_t>(a.target) & 15) == 0);
+
+  // ---- pass 1: max, sum exp, and the KL sums ----
+  float m = -INFINITY, s = 0.0f;
+  float sq = 0.0f, sqlogq = 0.0f, sqx = 0.0f;
+  for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+    Load4 x = load_group(Srow, g, V, true);
+    const int64_t e = 4 * g;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e + i < V) mx = fmaxf(mx, x.v[i]);
+    if (mx > m) {
+      s *= __expf(m - mx);
+      m = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e + i < V) s += __expf(x.v[i] - m);
+    if (HEAD == HEAD_KL) {
+      Load4 t = load_group(q, g, V, q_vec);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (e + i < V) {
+          const float qi = t.v[i];
+          sq += qi;
+          sqlogq += qi * __logf(fmaxf(qi, a.eps));
+          sqx += qi * x.v[i];
+        }
+      }
+    }
+  }
+  float s_label = 0.0f;
+  if (HEAD == HEAD_SEL && tid == 0) s_label = Srow[y];
+
+  // wave reduction, then across waves in a fixed order
+  {
+    float wm = wave_max(m);
+    float ws = (m == -INFINITY) ? 0.0f : s * __expf(m - wm);
+    ws = wave_sum(ws);
+    if (lane == 0) {
+      red[wave][0] = wm;
+      red[wave][1] = ws;
+    }
+    if (HEAD == HEAD_KL) {
+      float a0 = wave_sum(sq), a1 = wave_sum(sqlogq), a2 = wave_sum(sqx);
+      if (lane == 0) {
+        red[wave][2] = a0;
+        red[wave][3] = a1;
+        red[wave][4] = a2;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = red[0][0], Ssum = red[0][1];
+    float Q = 0.f, A = 0.f, B = 0.f;
+    for (int w = 1; w < kRowWaves; ++w) lse_merge(M, Ssum, red[w][0], red[w][1]);
+    if (HEAD == HEAD_KL)
+      for (int w = 0; w < kRowWaves; ++w) {
+        Q += red[w][2];
+        A += red[w][3];
+        B += red[w][4];
+      }
+    const float l = M + __logf(Ssum);
+    float rv;
+    if (HEAD == HEAD_KL)
+      rv = A - B + Q * l;  // sum_v q log q - q (S - l)
+    else
+      rv = s_label - l;    // log p(y)
+    a.rowval[gr] = rv;
+    bcast[0] = l;
+    bcast[1] = Q;
+  }
+  __syncthreads();
+  const float l = bcast[0];
+  const float g = a.sc->g;
+  float coef;  // dS = coef * (...) below
+  float Qr = 0.f;
+  if (HEAD == HEAD_KL) {
+    coef = g * a.inv_tau;
+    Qr = bcast[1];
+  } else {
+    const float w = a.weights ? a.weights[gr] : 1.0f;
+    coef = g * w * a.inv_tau;
+  }
+
+  // ---- pass 2: dZ = dS / tau, written in place ----
+  // The bf16 dZ of element v goes to bytes [2v, 2v + 2) of the row, i.e. over
+  // float slots that an earlier strip (or this strip, before the barrier)
+  // has already read. Each strip's loads complete before its barrier.
+  for (int64_t base = 0; base < ngroups; base += kStrip) {
+    Load4 xs[kUnroll];
+    Load4 qs[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = base + u * kRowThreads + tid;
+      if (g < ngroups) {
+        xs[u] = load_group(Srow, g, V, true);
+        if (HEAD == HEAD_KL) qs[u] = load_group(q, g, V, q_vec);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = base + u * kRowThreads + tid;
+      if (g >= ngroups) continue;
+      const int64_t e = 4 * g;
+      float d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __expf(xs[u].v[i] - l);
+        if (HEAD == HEAD_KL)
+          d[i] = coef * (Qr * p - qs[u].v[i]);
+        else
+          d[i] = coef * (((e + i) == y ? 1.0f : 0.0f) - p);
+      }
+      if (a.dz_bf16) {
+        if (e + 4 <= V) {
+          uint2 pk;
+          pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
+          pk.y = (unsigned)f2bf(d[2]) | ((unsigned)f2bf(d[3]) << 16);
+          *reinterpret_cast<uint2 *>(Zb + e) = pk;
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (e + i < V) Zb[e + i] = f2bf(d[i]);
+        }
+      } else {
+        if (e + 4 <= V) {
+          *reinterpret_cast<float4 *>(Srow + e) = make_float4(d[0], d[1], d[2], d[3]);
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (e + i < V) Srow[e + i] = d[i];
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void prep_kernel(const int64_t *labels, int64_t BT,
+                                                    int64_t ignore_index, int head,
+                                                    int reduction, int64_t V,
+                                                    DevScalars *sc) {
+  __shared__ long long part[1024];
+  long long n = 0;
+  if (labels) {
+    for (int64_t r = threadIdx.x; r < BT; r += blockDim.x) n += (labels[r] != ignore_index);
+  } else if (threadIdx.x == 0) {
+    n = BT;
+  }
+  part[threadIdx.x] = n;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long nv = part[0];
+    double g;
+    if (nv == 0) g = 0.0;
+    else if (reduction == 2) g = 1.0;                       // sum
+    else if (reduction == 1 && head == 0) g = 1.0 / (double(nv) * double(V));  // KL mean
+    else g = 1.0 / double(nv);                              // batchmean; selective mean
+    sc->n_valid = nv;
+    sc->g = float(g);
+    sc->pad = 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(1024) void finalize_kernel(const float *rowval,
+                                                        const float *weights, int64_t BT,
+                                                        const DevScalars *sc, float *loss) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t r = threadIdx.x; r < BT; r += blockDim.x) {
+    const double w = weights ? double(weights[r]) : 1.0;
+    acc += w * double(rowval[r]);
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = float(double(sc->g) * part[0]);
+}
+
+// db column sums: each x-thread owns two adjacent columns, the y-threads split
+// the rows, and the y-partials are added in a fixed order.
+constexpr int kColX = 64, kColY = 4;
+template <bool BF16>
+__global__ __launch_bounds__(kColX *kColY) void colsum_kernel(const void *dZ, int64_t ldz,
+                                                              int64_t rows, int64_t V,
+                                                              float *db, int accumulate) {
+  __shared__ float part[kColY][kColX][2];
+  const int tx = threadIdx.x, ty = threadIdx.y;
+  const int64_t v = (int64_t(blockIdx.x) * kColX + tx) * 2;
+  float s0 = 0.f, s1 = 0.f;
+  if (v < V) {
+    const bool two = v + 1 < V;
+    for (int64_t r = ty; r < rows; r += kColY) {
+      if (BF16) {
+        const unsigned short *row = static_cast<const unsigned short *>(dZ) + r * ldz;
+        s0 += __uint_as_float(unsigned(row[v]) << 16);
+        if (two) s1 += __uint_as_float(unsigned(row[v + 1]) << 16);
+      } else {
+        const float *row = static_cast<const float *>(dZ) + r * ldz;
+        s0 += row[v];
+        if (two) s1 += row[v + 1];
+      }
+    }
+  }
+  part[ty][tx][0] = s0;
+  part[ty][tx][1] = s1;
+  __syncthreads();
+  if (ty == 0 && v < V) {
+    float t0 = 0.f, t1 = 0.f;
+    for (int y = 0; y < kColY; ++y) {
+      t0 += part[y][tx][0];
+      t1 += part[y][tx][1];
+    }
+    db[v] = accumulate ? db[v] + t0 : t0;
+    if (v + 1 < V) db[v + 1] = accumulate ? db[v + 1] + t1 : t1;
+  }
+}
+
+__global__ void dx_reduce_kernel(const float *P, int64_t splits, int64_t M, int64_t N,
+                                 void *dX, int64_t ldo, int out_bf16) {
+  const int64_t n4 = N / 4;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= M * n4) return;
+  const int64_t m = i / n4, c = (i % n4) * 4;
+  float4 acc = *reinterpret_cast<const float4 *>(P + m * N + c);
+  for (int64_t s = 1; s < splits; ++s) {
+    float4 x = *reinterpret_cast<const float4 *>(P + (s * M + m) * N + c);
+    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  }
+  if (out_bf16) {
+    uint2 pk;
+    pk.x = (unsigned)f2bf(acc.x) | ((unsigned)f2bf(acc.y) << 16);
+    pk.y = (unsigned)f2bf(acc.z) | ((unsigned)f2bf(acc.w) << 16);
+    *reinterpret_cast<uint2 *>(static_cast<unsigned short *>(dX) + m * ldo + c) = pk;
+  } else {
+    *reinterpret_cast<float4 *>(static_cast<float *>(dX) + m * ldo + c) = acc;
+  }
+}
+
+__global__ void fill_kernel(float *p, int64_t n, float v) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+void launch_prep(const int64_t *labels, int64_t BT, int64_t ignore_index, int head,
+                 int reduction, int64_t V, DevScalars *sc, hipStream_t st) {
+  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, st, labels, BT, ignore_index,
+                     head, reduction, V, sc);
+}
+
+void launch_row(const RowArgs &a, hipStream_t st) {
+  if (a.rows <= 0) return;
+  if (a.head == HEAD_KL)
+    hipLaunchKernelGGL(row_kernel<HEAD_KL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(row_kernel<HEAD_SEL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+}
+
+void launch_colsum(const void *dZ, int dz_bf16, int64_t ldz, int64_t rows, int64_t V,
+                   float *db, int accumulate, hipStream_t st) {
+  const int64_t blocks = (V + 2 * kColX - 1) / (2 * kColX);
+  if (dz_bf16)
+    hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks), dim3(kColX, kColY), 0, st, dZ,
+                       ldz, rows, V, db, accumulate);
+  else
+    hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks), dim3(kColX, kColY), 0, st, dZ,
+                       ldz, rows, V, db, accumulate);
+}
+
+void launch_dx_reduce(const float *P, int64_t splits, int64_t M, int64_t N, void *dX,
+                      int64_t ldo, int out_bf16, hipStream_t st) {
+  const int64_t n = M * (N / 4);
+  if (n <= 0) return;
+  const int threads = 256;
+  hipLaunchKernelGGL(dx_reduce_kernel, dim3((n + threads - 1) / threads), dim3(threads), 0,
+                     st, P, splits, M, N, dX, ldo, out_bf16);
+}
+
+void launch_finalize(const float *rowval, const float *weights, int64_t BT,
+                     const DevScalars *sc, float *loss, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, rowval, weights, BT, sc,
+                     loss);
+}
+
+void launch_fill(float *p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, st, p, n, v);
+}
+
+}  // namespace fll

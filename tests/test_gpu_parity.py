@@ -1,0 +1,207 @@
+"""Parity of the HIP path with the CPU oracle, element by element.
+
+Sizes are chosen so the oracle finishes in seconds while the GPU kernels
+still run several 256 x 256 tiles with ragged tails in every dimension:
+H = 264 and 136 are not multiples of the 64-wide K-step or the 256-wide
+tile, V = 1000 / 777 / 4099 leave partial vocabulary tiles (777 is odd, so
+rows are not 16-byte multiples), and BT = 300 / 520 leave a partial last
+token chunk.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "cfg1-tiny-fp32-kl": workloads.CONFIGS[1],
+    "kl-bf16-ragged-trainable-bias": workloads.small_case(
+        BT=300, H=264, V=1000, dtype="bf16", head="kl", has_bias=True, compute_dW=True,
+        compute_db=True, temperature=2.0, ignore_frac=0.1, reduction="batchmean",
+        x_std=1.0, w_std=0.05, seed=11),
+    "sel-bf16-odd-vocab-trainable": workloads.small_case(
+        BT=520, H=136, V=777, dtype="bf16", head="selective", has_bias=True,
+        compute_dW=True, compute_db=True, reduction="mean", ignore_frac=0.05,
+        w_std=0.05, seed=12),
+    "sel-bf16-frozen-sum-two-vocab-chunks": workloads.small_case(
+        BT=300, H=256, V=4099, dtype="bf16", head="selective", reduction="sum",
+        temperature=0.5, w_std=0.02, seed=13),
+    "kl-bf16-mean-no-labels": workloads.small_case(
+        BT=257, H=64, V=2048, dtype="bf16", head="kl", reduction="mean", with_labels=False,
+        compute_dW=True, w_std=0.05, seed=14),
+    "sel-fp32-trainable": workloads.small_case(
+        BT=130, H=72, V=333, dtype="fp32", head="selective", has_bias=True,
+        compute_dW=True, compute_db=True, reduction="batchmean", x_std=1.0, w_std=0.1,
+        seed=15),
+    "kl-fp32-sum-ignored": workloads.small_case(
+        BT=100, H=40, V=515, dtype="fp32", head="kl", reduction="sum", ignore_frac=0.2,
+        compute_dW=True, x_std=1.0, w_std=0.1, temperature=0.75, seed=16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_parity(name):
+    case = SMALL[name]
+    print(f"[parity] {name} {case}", flush=True)
+    inp = H.make(case)
+    out = H.run_gpu(inp, case)
+    ref = H.run_oracle(inp, case)
+    H.compare_full(out, ref, case)
+
+
+def test_unnormalised_target():
+    # target rows summing to 1.3: the exact gradient uses Q_r = sum_v q_rv
+    case = workloads.small_case(BT=96, H=64, V=300, dtype="fp32", head="kl",
+                                compute_dW=True, reduction="batchmean", x_std=1.0,
+                                w_std=0.1, seed=21)
+    inp = H.make(case)
+    inp["target"] = inp["target"] * 1.3
+    H.compare_full(H.run_gpu(inp, case), H.run_oracle(inp, case), case)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_all_rows_ignored(dtype):
+    case = workloads.small_case(BT=64, H=32, V=100, dtype=dtype, head="selective",
+                                has_bias=True, compute_dW=True, compute_db=True, seed=22)
+    inp = H.make(case)
+    inp["labels"][:] = case.ignore_index
+    out = H.run_gpu(inp, case)
+    assert float(out["loss"]) == 0.0
+    for k in ("dX", "dW", "db", "per_row"):
+        assert torch.count_nonzero(out[k]).item() == 0, k
+
+
+@pytest.mark.parametrize("head", ["kl", "selective"])
+def test_empty_batch(head):
+    import lm_head_projection_token_amd as fll
+
+    dev = "cuda:0"
+    X = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    W = torch.randn(50, 64, device=dev).to(torch.bfloat16)
+    b = torch.zeros(50, dtype=torch.bfloat16, device=dev)
+    kw = dict(labels=torch.empty(0, dtype=torch.int64, device=dev))
+    if head == "kl":
+        kw["target"] = torch.empty(0, 50, device=dev)
+    out = fll.fused_lm_head_loss(X, W, b, head=head, compute_dW=True, compute_db=True, **kw)
+    torch.cuda.synchronize()
+    assert float(out["loss"]) == 0.0
+    assert out["dX"].shape == (0, 64)
+    assert torch.count_nonzero(out["dW"]).item() == 0
+    assert torch.count_nonzero(out["db"]).item() == 0
+
+
+@pytest.mark.parametrize("head", ["kl", "selective"])
+def test_single_token_vocabulary(head):
+    # V = 1: log p = 0 for every row, so the loss and every gradient vanish.
+    case = workloads.small_case(BT=40, H=16, V=1, dtype="bf16", head=head,
+                                compute_dW=True, seed=23)
+    inp = H.make(case)
+    out = H.run_gpu(inp, case)
+    ref = H.run_oracle(inp, case)
+    assert abs(float(out["loss"]) - ref["loss"]) <= 1e-6
+    assert torch.count_nonzero(out["dX"]).item() == 0
+
+
+def test_out_of_range_label_is_nan_not_a_fault():
+    case = workloads.small_case(BT=64, H=32, V=100, dtype="bf16", head="selective",
+                                compute_dW=True, seed=24)
+    inp = H.make(case)
+    inp["labels"][5] = 100   # == V
+    inp["labels"][9] = -7    # negative, not ignore_index
+    out = H.run_gpu(inp, case)
+    assert np.isnan(float(out["loss"]))
+    per = out["per_row"].cpu()
+    assert torch.isnan(per[5]) and torch.isnan(per[9])
+    assert torch.count_nonzero(out["dX"][5]).item() == 0
+    assert torch.isfinite(out["dX"]).all() and torch.isfinite(out["dW"]).all()
+
+
+# --------------------------------------------------------------------------
+# bit-identity and determinism
+# --------------------------------------------------------------------------
+
+BITCASE = workloads.small_case(BT=600, H=136, V=1000, dtype="bf16", head="kl",
+                               has_bias=True, compute_dW=True, compute_db=True,
+                               temperature=2.0, ignore_frac=0.1, w_std=0.05, seed=31)
+
+
+def test_dx_bit_identical_frozen_vs_trainable():
+    # LoRA normalization page, Test Validation: the input gradient is exactly
+    # equal whether or not the weight gradients are formed.
+    inp = H.make(BITCASE)
+    trainable = H.run_gpu(inp, BITCASE)
+    frozen_case = BITCASE.replace(compute_dW=False, compute_db=False)
+    frozen = H.run_gpu(inp, frozen_case)
+    assert torch.equal(trainable["dX"], frozen["dX"])
+    assert torch.equal(trainable["loss"], frozen["loss"])
+    assert frozen["dW"] is None and frozen["db"] is None
+
+
+def test_frozen_head_leaves_dw_untouched():
+    # With compute_dW = compute_db = 0 the call may be handed dW / db buffers
+    # and must not touch them [frozen lm_head GRPO page, Summary].
+    import lm_head_projection_token_amd as fll
+
+    case = BITCASE.replace(compute_dW=False, compute_db=False)
+    inp = H.make(case)
+    dev = "cuda:0"
+    X, W, b = (inp[k].to(dev) for k in ("X", "W", "b"))
+    prob = fll.make_problem(case.BT, case.H, case.V, dtype="bf16", head="kl", has_bias=True,
+                            temperature=case.temperature)
+    plan = fll.fll_plan(prob)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    dW = torch.full((case.V, case.H), 7.25, device=dev)
+    db = torch.full((case.V,), -3.5, device=dev)
+    loss = torch.empty((), device=dev)
+    dX = torch.empty_like(X)
+    fll.fll_fwd_bwd(plan, X=X, W=W, b=b, labels=inp["labels"].to(dev),
+                    target=inp["target"].to(dev), dX=dX, dW=dW, db=db, loss=loss,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((dW == 7.25).all()) and bool((db == -3.5).all())
+    assert torch.isfinite(dX).all() and torch.isfinite(loss)
+
+
+def test_chunk_size_does_not_change_dx():
+    inp = H.make(BITCASE)
+    base = H.run_gpu(inp, BITCASE)
+    assert base["plan"].n_chunks >= 2
+    for C in (100, 37, 600):
+        other = H.run_gpu(inp, BITCASE, chunk_rows=C)
+        assert other["plan"].chunk_rows == C
+        assert torch.equal(base["dX"], other["dX"]), C
+        assert torch.equal(base["per_row"], other["per_row"]), C
+        # dW / db are sums over chunks: equal up to fp32 reassociation
+        torch.testing.assert_close(other["dW"], base["dW"], rtol=1e-5,
+                                   atol=1e-6 * float(base["dW"].abs().max()))
+        torch.testing.assert_close(other["db"], base["db"], rtol=1e-5,
+                                   atol=1e-6 * float(base["db"].abs().max()))
+
+
+def test_repeated_calls_are_bitwise_equal():
+    inp = H.make(BITCASE)
+    a = H.run_gpu(inp, BITCASE)
+    b = H.run_gpu(inp, BITCASE)
+    for k in ("loss", "dX", "dW", "db", "per_row"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_temperature_power_of_two_identity():
+    # (X W^T + b) / 2 == X (W / 2)^T + b / 2 exactly in the GEMM's fp32
+    # accumulation, so dX agrees bitwise and dW(tau) = dW'(1) / tau.
+    case = workloads.small_case(BT=300, H=136, V=1000, dtype="bf16", head="selective",
+                                has_bias=True, compute_dW=True, compute_db=True,
+                                temperature=2.0, w_std=0.05, seed=32)
+    inp = H.make(case)
+    a = H.run_gpu(inp, case)
+    inp2 = dict(inp)
+    inp2["W"] = (inp["W"].float() / 2).to(torch.bfloat16)
+    inp2["b"] = (inp["b"].float() / 2).to(torch.bfloat16)
+    b = H.run_gpu(inp2, case.replace(temperature=1.0))
+    assert torch.equal(a["loss"], b["loss"])
+    torch.testing.assert_close(a["dX"].float(), b["dX"].float(), rtol=0, atol=0)
+    torch.testing.assert_close(a["dW"], b["dW"] / 2, rtol=0, atol=0)
