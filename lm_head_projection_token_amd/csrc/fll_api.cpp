@@ -55,8 +55,8 @@ int check_problem(const fll_problem *p) {
   if (p->H < 8 || p->H % 8 != 0)
     return fail(FLL_ERR_INVALID_ARG, "H must be a positive multiple of 8 (got %lld)",
                 (long long)p->H);
-  if (p->V > (int64_t(1) << 31) || p->H > (int64_t(1) << 20))
-    return fail(FLL_ERR_INVALID_ARG, "V or H too large");
+  if (p->V > (int64_t(1) << 21) - 64 || p->H > (int64_t(1) << 20))
+    return fail(FLL_ERR_INVALID_ARG, "V (max 2^21 - 64) or H (max 2^20) too large");
   for (int f : {p->has_bias, p->compute_dW, p->compute_db})
     if (f != 0 && f != 1) return fail(FLL_ERR_INVALID_ARG, "flags must be 0 or 1");
   if (p->compute_db && !p->has_bias)

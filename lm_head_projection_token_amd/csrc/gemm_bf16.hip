@@ -4,30 +4,42 @@
 // the forward logits and the grad_logits^T @ hidden weight gradient;
 // FusedLinearKLDivLoss page, Details: fp32 weight-gradient accumulation]:
 //
-//   logits  S  = (X W^T + b) / tau     A = X   [C x H]  K-contiguous
-//                                      B = W   [V x H]  K-contiguous
-//   dX      dX = dZ W                  A = dZ  [C x V]  K-contiguous
-//                                      B = W   (K = V)  N-contiguous
-//   dW      dW (+)= dZ^T X             A = dZ^T (K = C) M-contiguous
-//                                      B = X   (K = C)  N-contiguous
+//   logits  S  = (X W^T + b) / tau     A = X    [C x H]   K-contiguous
+//                                      B = W    [V x H]   K-contiguous
+//   dX      dX = dZ W                  A = dZ   [C x V]   K-contiguous
+//                                      B = W    (K = V)   N-contiguous
+//   dW      dW (+)= dZ^T X             A = dZ^T (K = C)   M-contiguous
+//                                      B = X    (K = C)   N-contiguous
 //
 // One kernel template serves all three. A workgroup of 256 threads (four
 // wavefronts in a 2 x 2 grid) computes a 256 x 256 tile; each wavefront owns
 // 128 x 128 of it as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 with fp32
-// accumulators. Both operands are staged through LDS in a K-contiguous
-// layout, 64 K-values (8 chunks of 16 bytes) per row, with the chunk index
-// XOR-swizzled by the row so that the 16-byte fragment reads and the staging
-// writes are free of bank conflicts. Operands that are not K-contiguous in
-// memory are loaded as 8 x 8 blocks of 16-byte rows and transposed in
-// registers before the LDS write. Two LDS stages (128 KB of the 160 KB per
-// CU) let the global loads of the next K-step overlap the MFMAs of this one,
-// with one barrier per K-step.
+// accumulators (256 AGPRs).
 //
-// Workgroups are dispatched round-robin over the 8 XCDs; the tile order is
-// remapped so that each XCD receives a contiguous run of tiles, and the run
-// walks the tile grid along the dimension whose operand panel it can share in
-// that XCD's L2.
+// Staging. Each K-step of 32 moves a 256 x 32 slice of each operand from
+// global memory straight into LDS with buffer_load_dwordx4 ... lds (no
+// registers, no LDS write instructions). Four LDS stages of 32 KB are in
+// flight, so a slice is requested about two and a half K-steps before its
+// MFMAs run. The buffer descriptors give zero fill for rows past the end of
+// an operand; K-chunks past the end are pointed outside the descriptor's
+// range and read as zero as well.
+//   K-contiguous operands keep their memory layout in LDS: 256 rows of 64
+//   bytes, 16-byte chunks XOR-swizzled by row, read with ds_read_b128.
+//   MN-contiguous operands also keep their layout: 32 K-rows of 512 bytes,
+//   chunks XOR-swizzled by K-row, read with ds_read_b64_tr_b16, whose
+//   16-lane transpose hands each lane four consecutive K-values of its own
+//   column; two such reads form one MFMA operand of eight K-values.
+// MFMA fragments are double-buffered in registers: the reads for the next
+// 16-deep half-step are issued between the MFMAs of the current one.
+//
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs. The
+// logical tile sequence walks groups of G tile-rows (tile-row fastest inside
+// a group) and each XCD receives a contiguous run of it, so the tiles that
+// run together on one XCD form a compact G x (32 / G) block and share their
+// operand panels in that XCD's L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "fll_internal.h"
 
@@ -35,90 +47,126 @@ namespace fll {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int kThreads = 256;
-constexpr int kChunks = BK / 8;           // 16-byte chunks per LDS row
-constexpr int kTileChunks = 256 * kChunks;  // per operand per stage
+constexpr int kOperandBytes = 256 * BK * 2;     // 16 KB per operand per stage
+constexpr int kStageBytes = 2 * kOperandBytes;  // 32 KB
+constexpr int kLoadsPerStage = 8;               // per thread: 4 for A, 4 for B
+constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
+constexpr unsigned kMaxRecords = 0x7fffffffu;
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_idx(int r, int c) { return r * kChunks + (c ^ swz(r)); }
-
-// Zero the bf16 lanes of a 16-byte chunk at element positions >= keep.
-__device__ __forceinline__ u32x4 keep_first(u32x4 v, int keep) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int e0 = 2 * d, e1 = 2 * d + 1;
-    unsigned int w = v[d];
-    if (e0 >= keep) w &= 0xffff0000u;
-    if (e1 >= keep) w &= 0x0000ffffu;
-    v[d] = w;
-  }
-  return v;
+// Swizzles of the 16-byte chunk index. K-contiguous tiles (4 chunks per row):
+// the 32 rows that one ds_read_b128 touches spread over all banks.
+// MN-contiguous tiles (32 chunks per K-row): the four K-rows that a 16-lane
+// group of ds_read_b64_tr_b16 touches land on distinct banks.
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int swz_mn(int k) {
+  return (0x6ca0 >> ((k & 3) * 4)) & 15;  // {0, 10, 12, 6}[k & 3]
 }
 
-// Operand rows of the tile come from memory with K contiguous: element
-// (row, k) at p[row * ld + k]. Thread t moves chunk t % 8 of rows t / 8 + 32 i.
-struct StageK {
-  __device__ __forceinline__ static void load(u32x4 (&reg)[8], const unsigned short *p,
-                                              int64_t ld, int64_t row0, int64_t nrows,
-                                              int64_t k0, int64_t kend, int t) {
-    const int c = t & 7;
-    const int64_t k = k0 + c * 8;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes > int64_t(kMaxRecords) ? int64_t(kMaxRecords) : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, LDS_AS void *dst,
+                                           unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+// ---- K-contiguous operand: element (row, k) at p[row * ld + k] -------------
+struct OpK {
+  const unsigned short *p;
+  int64_t ld, row0, nrows;
+  unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
+  int kc[4];         // their K offsets within the slice
+  unsigned fa[2];    // fragment read byte offsets (half-step 0 and 1)
+
+  __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
+                                       int64_t nrows_, int wave, int lane, int wr) {
+    p = p_;
+    ld = ld_;
+    row0 = row0_;
+    nrows = nrows_;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = row0 + (t >> 3) + 32 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < nrows && k < kend) {
-        v = *reinterpret_cast<const u32x4 *>(p + row * ld + k);
-        if (k + 8 > kend) v = keep_first(v, int(kend - k));
-      }
-      reg[i] = v;
+    for (int i = 0; i < 4; ++i) {
+      const int r = (wave * 4 + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_k(r);
+      voff[i] = unsigned((int64_t(r) * ld + 8 * c) * 2);
+      kc[i] = 8 * c;
+    }
+    const int r = wr + (lane & 31);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * h + (lane >> 5);
+      fa[h] = unsigned(r * 64 + 16 * (c ^ swz_k(r)));
     }
   }
-  __device__ __forceinline__ static void store(u32x4 *lds, const u32x4 (&reg)[8], int t) {
-    const int c = t & 7;
+  __device__ __forceinline__ void issue(LDS_AS char *stage, int wave, int64_t k0,
+                                        int64_t kend) const {
+    const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lds[lds_idx((t >> 3) + 32 * i, c)] = reg[i];
+    for (int i = 0; i < 4; ++i) {
+      const unsigned v = (k0 + kc[i] < kend) ? voff[i] : kOOB;
+      load_lds16(r, stage + (wave * 4 + i) * 1024, v);
+    }
+  }
+  // Fragment of block i (rows wr + 32 i ...), half-step h.
+  __device__ __forceinline__ bf16x8 frag(const LDS_AS char *stage, int i, int h) const {
+    const u32x4 v = *reinterpret_cast<const LDS_AS u32x4 *>(stage + fa[h] + i * 2048);
+    return __builtin_bit_cast(bf16x8, v);
   }
 };
 
-// Operand rows of the tile are contiguous in memory, K is the slow index:
-// element (row, k) at p[k * ld + row]. Thread t loads an 8 x 8 block (8
-// K-values of 8 consecutive rows) and transposes it in registers.
-// A partial 8-row chunk at the end of the rows is read whole: callers
-// guarantee the row pitch covers it, and rows >= nrows only feed output
-// rows or columns that are never stored.
-struct StageMN {
-  __device__ __forceinline__ static void load(u32x4 (&reg)[8], const unsigned short *p,
-                                              int64_t ld, int64_t row0, int64_t nrows,
-                                              int64_t k0, int64_t kend, int t) {
-    const int64_t row = row0 + (t & 31) * 8;
-    const int64_t kb = k0 + (t >> 5) * 8;
+// ---- MN-contiguous operand: element (row, k) at p[k * ld + row] ------------
+struct OpMN {
+  const unsigned short *p;
+  int64_t ld, col0;
+  unsigned voff[4];  // byte offsets of this thread's 4 chunks from (k0, col0)
+  unsigned fb[4];    // transpose-read byte offsets, block i (half-step 0, h 0)
+
+  __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t col0_,
+                                       int wave, int lane, int wr) {
+    p = p_;
+    ld = ld_;
+    col0 = col0_;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t k = kb + j;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < nrows && k < kend) v = *reinterpret_cast<const u32x4 *>(p + k * ld + row);
-      reg[j] = v;
+    for (int i = 0; i < 4; ++i) {
+      const int kr = (wave * 4 + i) * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swz_mn(kr);
+      voff[i] = unsigned((int64_t(kr) * ld + 8 * c) * 2);
+    }
+    // 16-lane group G, lane q: K-row 8 (G >> 1) + (q >> 2), columns
+    // wr + 32 i + 16 (G & 1) + 4 (q & 3) .. + 3.
+    const int G = lane >> 4, q = lane & 15;
+    const int k = 8 * (G >> 1) + (q >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = wr + 32 * i + 16 * (G & 1) + 4 * (q & 3);
+      const int c = col >> 3, half = (col >> 2) & 1;
+      fb[i] = unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
     }
   }
-  __device__ __forceinline__ static void store(u32x4 *lds, const u32x4 (&in)[8], int t) {
-    const int rb = (t & 31) * 8;
-    const int c = t >> 5;
+  __device__ __forceinline__ void issue(LDS_AS char *stage, int wave, int64_t k0,
+                                        int64_t kend) const {
+    const __amdgpu_buffer_rsrc_t r = rsrc(p + k0 * ld + col0, ((kend - k0) * ld - col0) * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = i >> 1;
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned int x = in[2 * e][d], y = in[2 * e + 1][d];
-        o[e] = (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-      }
-      lds[lds_idx(rb + i, c)] = o;
-    }
+    for (int i = 0; i < 4; ++i) load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
+  }
+  __device__ __forceinline__ bf16x8 frag(const LDS_AS char *stage, int i, int h) const {
+    // half-step h covers K-rows 16 h ...; the two reads cover K +0..3 and +4..7
+    const LDS_AS char *b = stage + fb[i] + h * 16 * 512;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(b));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(b + 4 * 512));
+    const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
   }
 };
 
@@ -130,7 +178,7 @@ struct GemmDesc {
   int64_t M, N, K;
   int64_t split_len;  // K per split
   int tiles_m, tiles_n, splits;
-  int m_fastest;      // tile order: 1 = walk M first (share B), 0 = walk N first
+  int group;          // tile-rows per group of the tile order
 };
 
 // Logits epilogue: S = (acc + b[n]) * inv_tau, fp32.
@@ -181,12 +229,15 @@ struct EpiDw {
   }
 };
 
-template <class SA, class SB, class Epi>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) {
-  __shared__ u32x4 lds[2][2][kTileChunks];  // [stage][A, B]: 128 KB
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
 
-  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a
-  // contiguous run of the logical tile sequence.
+template <bool A_K, bool B_K, class Epi>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];  // 128 KB
+  LDS_AS char *lds = (LDS_AS char *)smem;
+
+  // ---- tile: XCD-aware remap, then grouped order ----
   const int T = gridDim.x;
   const int b = blockIdx.x;
   const int xcd = b & 7, j = b >> 3;
@@ -195,14 +246,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int tiles_mn = d.tiles_m * d.tiles_n;
   const int split = tl / tiles_mn;
   const int tmn = tl - split * tiles_mn;
-  int tm, tn;
-  if (d.m_fastest) {
-    tm = tmn % d.tiles_m;
-    tn = tmn / d.tiles_m;
-  } else {
-    tn = tmn % d.tiles_n;
-    tm = tmn / d.tiles_n;
-  }
+  const int gsz = d.group * d.tiles_n;
+  const int grp = tmn / gsz;
+  const int first_m = grp * d.group;
+  const int gm = min(d.group, d.tiles_m - first_m);
+  const int local = tmn - grp * gsz;
+  const int tm = first_m + local % gm;
+  const int tn = local / gm;
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t kbeg = int64_t(split) * d.split_len;
   const int64_t kend = min(d.K, kbeg + d.split_len);
@@ -210,6 +260,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+
+  typename std::conditional<A_K, OpK, OpMN>::type opa;
+  typename std::conditional<B_K, OpK, OpMN>::type opb;
+  if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, wave, lane, wm * 128);
+  else opa.init(d.A, d.lda, m0, wave, lane, wm * 128);
+  if constexpr (B_K) opb.init(d.B, d.ldb, n0, d.N, wave, lane, wn * 128);
+  else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -219,54 +276,82 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][k][e] = 0.0f;
 
+  // LDS reads per half-step: one per K-contiguous block, two per MN block
+  constexpr int kReadsPerHalf = (A_K ? 4 : 8) + (B_K ? 4 : 8);
   const int nkt = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
-  u32x4 ra[8], rb[8];
-  if (nkt > 0) {
-    SA::load(ra, d.A, d.lda, m0, d.M, kbeg, kend, t);
-    SB::load(rb, d.B, d.ldb, n0, d.N, kbeg, kend, t);
-    SA::store(lds[0][0], ra, t);
-    SB::store(lds[0][1], rb, t);
-  }
-  __syncthreads();
+  auto stageA = [&](int s) { return lds + (s % NSTAGE) * kStageBytes; };
+  auto stageB = [&](int s) { return lds + (s % NSTAGE) * kStageBytes + kOperandBytes; };
+  auto issue = [&](int s) {
+    const int64_t k0 = kbeg + int64_t(s) * BK;
+    opa.issue(stageA(s), wave, k0, kend);
+    opb.issue(stageB(s), wave, k0, kend);
+  };
 
-  const int frow = lane & 31;   // fragment row within a 32-block
-  const int fhalf = lane >> 5;  // which 8 of the 16 K-values
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      const int64_t k0 = kbeg + int64_t(kt + 1) * BK;
-      SA::load(ra, d.A, d.lda, m0, d.M, k0, kend, t);
-      SB::load(rb, d.B, d.ldb, n0, d.N, k0, kend, t);
-    }
-    const u32x4 *la = lds[cur][0];
-    const u32x4 *lb = lds[cur][1];
+  if (nkt > 0) {
+    // prologue: three stages in flight, wait for the first
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks * 2 + fhalf;
-      bf16x8 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x4 x = la[lds_idx(wm * 128 + i * 32 + frow, c)];
-        af[i] = __builtin_bit_cast(bf16x8, x);
-        u32x4 y = lb[lds_idx(wn * 128 + i * 32 + frow, c)];
-        bf[i] = __builtin_bit_cast(bf16x8, y);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[k], acc[i][k], 0, 0, 0);
-    }
-    if (more) {
-      SA::store(lds[cur ^ 1][0], ra, t);
-      SB::store(lds[cur ^ 1][1], rb, t);
-    }
-    __syncthreads();
+    for (int s = 0; s < NSTAGE - 1; ++s) issue(s);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
   }
+
+  bf16x8 fa[2][4], fb[2][4];
+  if (nkt > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[0][i] = opa.frag(stageA(0), i, 0);
+      fb[0][i] = opb.frag(stageB(0), i, 0);
+    }
+  }
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    // [A] request stage kt + 3 (past the end: zero-filled, never read)
+    issue(kt + NSTAGE - 1);
+    // [B] half-step 0 MFMAs; read half-step 1 fragments of stage kt
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[1][i] = opa.frag(stageA(kt), i, 1);
+      fb[1][i] = opb.frag(stageB(kt), i, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][k], acc[i][k], 0, 0, 0);
+    // interleave the 8 stage loads and the fragment reads with the 16 MFMAs
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      if (x < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsPerHalf / 16 + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+
+    // [C] stage kt + 1 complete in LDS for every wave
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+
+    // [D] half-step 1 MFMAs; read half-step 0 fragments of stage kt + 1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[0][i] = opa.frag(stageA(kt + 1), i, 0);
+      fb[0][i] = opb.frag(stageB(kt + 1), i, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][k], acc[i][k], 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsPerHalf / 16 + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Accumulator layout of the 32 x 32 block: lane l holds column l % 32;
   // register r holds row 8 (r / 4) + 4 (l / 32) + r % 4.
+  const int fhalf = lane >> 5;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t n = n0 + wn * 128 + k * 32 + (lane & 31);
@@ -285,14 +370,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 
 inline int cdiv(int64_t a, int64_t b) { return int((a + b - 1) / b); }
 
-template <class SA, class SB, class Epi>
+template <bool A_K, bool B_K, class Epi>
 void launch(const GemmDesc &d0, const Epi &epi, hipStream_t st) {
   GemmDesc d = d0;
   d.tiles_m = cdiv(d.M, BM);
   d.tiles_n = cdiv(d.N, BN);
   const int64_t blocks = int64_t(d.tiles_m) * d.tiles_n * d.splits;
   if (blocks <= 0) return;
-  hipLaunchKernelGGL((gemm_kernel<SA, SB, Epi>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_kernel<A_K, B_K, Epi>), dim3(unsigned(blocks)), dim3(kThreads), 0,
                      st, d, epi);
 }
 
@@ -311,9 +396,9 @@ void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
   d.K = K;
   d.split_len = K;
   d.splits = 1;
-  d.m_fastest = 1;  // tiles sharing a W panel run together
+  d.group = 8;
   EpiLogits e{S, lds, static_cast<const unsigned short *>(b), inv_tau};
-  launch<StageK, StageK>(d, e, st);
+  launch<true, true>(d, e, st);
 }
 
 void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw, void *dX,
@@ -329,9 +414,9 @@ void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw, voi
   d.K = K;
   d.split_len = splits > 1 ? split_len : K;
   d.splits = int(splits);
-  d.m_fastest = 1;  // tiles sharing a W panel run together
+  d.group = 8;
   EpiDx e{static_cast<unsigned short *>(dX), ldo, splits > 1 ? partial : nullptr, M, N};
-  launch<StageK, StageMN>(d, e, st);
+  launch<true, false>(d, e, st);
 }
 
 void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx, float *dW,
@@ -346,9 +431,9 @@ void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx, flo
   d.K = K;
   d.split_len = K;
   d.splits = 1;
-  d.m_fastest = 0;  // tiles sharing a dZ^T panel run together
+  d.group = 4;
   EpiDw e{dW, N, accumulate};
-  launch<StageMN, StageMN>(d, e, st);
+  launch<false, false>(d, e, st);
 }
 
 }  // namespace fll

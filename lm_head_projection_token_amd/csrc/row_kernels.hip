@@ -51,6 +51,13 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
   return (unsigned short)(u >> 16);
 }
 
+// bf16 dZ rows are read by the GEMMs in 8-element chunks; the slots from V to
+// the next multiple of 8 are zeroed so a partial last chunk adds nothing.
+__device__ __forceinline__ void zero_pad(unsigned short *Zb, int64_t V, int tid) {
+  const int64_t pad = (8 - (V & 7)) & 7;
+  if (tid < pad) Zb[V + tid] = 0;
+}
+
 struct Load4 {
   float v[4];
 };
@@ -104,6 +111,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
       }
     }
     if (tid == 0) a.rowval[gr] = bad_label ? NAN : 0.0f;
+    if (a.dz_bf16) zero_pad(Zb, V, tid);
     return;
   }
 
@@ -246,6 +254,8 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
       }
     }
   }
+  // Every read of this row finished before the last strip's barrier.
+  if (a.dz_bf16) zero_pad(Zb, V, tid);
 }
 
 __global__ __launch_bounds__(1024) void prep_kernel(const int64_t *labels, int64_t BT,
