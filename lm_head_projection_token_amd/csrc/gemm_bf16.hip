@@ -160,11 +160,17 @@ struct OpMN {
 #pragma unroll
     for (int i = 0; i < 4; ++i) load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
   }
+  // The transposing reads are issued as inline assembly: issued through the
+  // builtin, the compiler cannot tell them apart from the in-flight LDS-DMA
+  // stage loads and drains the whole load queue (vmcnt(0)) before each one.
+  // Their results are therefore not tracked by the compiler: every consumer
+  // first passes the fragment through lds_wait() below.
   __device__ __forceinline__ bf16x8 frag(const LDS_AS char *stage, int i, int h) const {
     // half-step h covers K-rows 16 h ...; the two reads cover K +0..3 and +4..7
     const LDS_AS char *b = stage + fb[i] + h * 16 * 512;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(b));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(b + 4 * 512));
+    i16x4 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(b));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(b));
     const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, v);
   }
@@ -228,6 +234,12 @@ struct EpiDw {
     *p = accumulate ? *p + v : v;
   }
 };
+
+// Wait for every outstanding LDS read and tie the fragments to the wait, so
+// no MFMA that consumes them can be scheduled above it.
+__device__ __forceinline__ void lds_wait(bf16x8 (&f)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+}
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
@@ -305,9 +317,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   }
 
   for (int kt = 0; kt < nkt; ++kt) {
-    // [A] request stage kt + 3 (past the end: zero-filled, never read)
-    issue(kt + NSTAGE - 1);
-    // [B] half-step 0 MFMAs; read half-step 1 fragments of stage kt
+    // Fragments of half-step 0 (read during the previous half-step) are ready.
+    lds_wait(fa[0]);
+    lds_wait(fb[0]);
+    // [B] half-step 0 MFMAs; meanwhile request the A slice of stage kt + 3
+    // (past the end: zero-filled, never read) and read the half-step 1
+    // fragments of stage kt.
+    {
+      const int64_t k0 = kbeg + int64_t(kt + NSTAGE - 1) * BK;
+      opa.issue(stageA(kt + NSTAGE - 1), wave, k0, kend);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       fa[1][i] = opa.frag(stageA(kt), i, 1);
@@ -318,19 +337,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][k], acc[i][k], 0, 0, 0);
-    // interleave the 8 stage loads and the fragment reads with the 16 MFMAs
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      if (x < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsPerHalf / 16 + 1, 0);
+      if ((x & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     }
 
-    // [C] stage kt + 1 complete in LDS for every wave
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
+    // [C] stage kt + 1 complete in LDS for every wave: of the loads issued so
+    // far only stage kt + 2 (8 per thread) and the A half of stage kt + 3 (4)
+    // may still be in flight.
+    lds_wait(fa[1]);
+    lds_wait(fb[1]);
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     __builtin_amdgcn_s_barrier();
 
-    // [D] half-step 1 MFMAs; read half-step 0 fragments of stage kt + 1
+    // [D] half-step 1 MFMAs; request the B slice of stage kt + 3 and read the
+    // half-step 0 fragments of stage kt + 1.
+    {
+      const int64_t k0 = kbeg + int64_t(kt + NSTAGE - 1) * BK;
+      opb.issue(stageB(kt + NSTAGE - 1), wave, k0, kend);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       fa[0][i] = opa.frag(stageA(kt + 1), i, 0);
@@ -343,7 +370,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
         acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][k], acc[i][k], 0, 0, 0);
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsPerHalf / 16 + 1, 0);
+      if ((x & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     }
   }
