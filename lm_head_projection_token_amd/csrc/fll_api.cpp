@@ -79,7 +79,8 @@ void layout(fll_plan_t *pl, int64_t C) {
   int64_t splits = std::min<int64_t>(4, std::max<int64_t>(1, cdiv(p.V, 16384)));
   pl->dx_split_len = rup(cdiv(p.V, splits), 64);
   pl->dx_splits = cdiv(p.V, pl->dx_split_len);
-  pl->stat_tiles = 0;
+  // per-row (max, sum exp) of every 128-column block, from the bf16 logits GEMM
+  pl->stat_tiles = p.dtype == FLL_BF16 ? cdiv(p.V, 128) : 0;
   size_t off = 0;
   pl->off_logits = off;
   off = align256(off + size_t(C) * size_t(pl->s_pitch) * 4);
@@ -258,6 +259,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   float *S = reinterpret_cast<float *>(ws + plan->off_logits);
   float *rowval = a.per_row ? a.per_row : reinterpret_cast<float *>(ws + plan->off_rowval);
   float *partial = reinterpret_cast<float *>(ws + plan->off_dx_partial);
+  float2 *stats = plan->stat_tiles ? reinterpret_cast<float2 *>(ws + plan->off_stats) : nullptr;
   auto *sc = reinterpret_cast<fll::DevScalars *>(ws + plan->off_scalars);
   const bool bf16 = p.dtype == FLL_BF16;
   const size_t esz = bf16 ? 2 : 4;
@@ -285,8 +287,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     {
       Probe pr(FLL_K_LOGITS, s);
       if (bf16)
-        fll::launch_logits_bf16(Xc, p.H, a.W, p.H, a.b, inv_tau, S, plan->s_pitch,
-                                rows, p.V, p.H, s);
+        fll::launch_logits_bf16(Xc, p.H, a.W, p.H, a.b, inv_tau, S, plan->s_pitch, stats,
+                                plan->stat_tiles, rows, p.V, p.H, s);
       else
         fll::launch_logits_f32(reinterpret_cast<const float *>(Xc), p.H,
                                static_cast<const float *>(a.W), p.H,
@@ -311,6 +313,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       ra.eps = p.eps;
       ra.sc = sc;
       ra.rowval = rowval;
+      ra.stats = stats;
+      ra.n_stat = plan->stat_tiles;
       Probe pr(FLL_K_ROW, s);
       fll::launch_row(ra, s);
     }

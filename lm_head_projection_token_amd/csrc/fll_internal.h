@@ -18,11 +18,12 @@ struct DevScalars {
 
 // S[m, n] = (sum_k X[m, k] W[n, k] + b[n]) * inv_tau for m < M, n < N.
 // X: [M x K] row pitch ldx; W: [N x K] row pitch ldw; S row pitch lds (floats).
-// If stats != nullptr, also writes per-(row, 256-column tile) max and
-// sum-exp partials: stats[(m * n_tiles + tile) * 2 + {0, 1}].
+// If stats != nullptr, also writes for every row m and 128-column block t
+// the block's max and sum of exp(S - max): stats[m * n_stat + t] = (max, sum),
+// n_stat = ceil(N / 128).
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
-                        const void *b, float inv_tau, float *S, int64_t lds,
-                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+                        const void *b, float inv_tau, float *S, int64_t lds, float2 *stats,
+                        int64_t n_stat, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 // dX = dZ W. dZ: bf16 [M x K] row pitch ldz (elements); W: [K x N] pitch ldw.
 // splits == 1: writes bf16 dX [M x N] (pitch ldo). splits > 1: writes fp32
@@ -57,7 +58,9 @@ void launch_prep(const int64_t *labels, int64_t BT, int64_t ignore_index,
                  int head, int reduction, int64_t V, DevScalars *sc,
                  hipStream_t st);
 
-// The fused row kernel over the rows [row0, row0 + rows) of one chunk.
+// The fused row kernel over the rows [row0, row0 + rows) of one chunk. With
+// stats it forms log-sum-exp from the logits GEMM's block statistics and
+// streams the logits once; without, it takes a first pass for max / sum exp.
 // S: the chunk's tempered logits (fp32, pitch s_pitch floats). On return the
 // first V entries of each row hold dZ = dS / tau: bf16 packed at the start of
 // the row (bf16 pitch 2 * s_pitch) when dz_bf16, else fp32 in place.
@@ -78,6 +81,8 @@ struct RowArgs {
   float eps;
   const DevScalars *sc;
   float *rowval;          // global [BT]
+  const float2 *stats;    // per-(row, 128-column block) (max, sum exp) or null
+  int64_t n_stat;         // blocks per row
 };
 void launch_row(const RowArgs &a, hipStream_t st);
 

@@ -33,11 +33,17 @@
 // 16-deep half-step are issued between the MFMAs of the current one.
 //
 // Tile order. Workgroups are dispatched round-robin over the 8 XCDs. The
-// logical tile sequence walks groups of G tile-rows (tile-row fastest inside
-// a group) and each XCD receives a contiguous run of it, so the tiles that
-// run together on one XCD form a compact G x (32 / G) block and share their
-// operand panels in that XCD's L2.
+// logical tile sequence walks groups of G tile-rows (or tile-columns), the
+// short side fastest inside a group; optionally each XCD first receives a
+// contiguous run of that sequence. Which combination keeps the most operand
+// slices in L2 (and shares MALL fills across XCDs) was measured per product
+// on the head shapes (C = 4096, H = 4096, V = 128256):
+//   logits: groups of 16 tile-rows in dispatch order (each XCD keeps two X
+//           panels resident while all XCDs stream the same W panels);
+//   dX:     groups of 4 tile-columns in dispatch order;
+//   dW:     groups of 8 tile-rows, one contiguous run per XCD.
 #include <hip/hip_runtime.h>
+#include <math.h>
 
 #include <type_traits>
 
@@ -48,15 +54,23 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
+#ifndef FLL_GEMM_STAGES
+#define FLL_GEMM_STAGES 4
+#endif
+constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = FLL_GEMM_STAGES;
 constexpr int kThreads = 256;
 constexpr int kOperandBytes = 256 * BK * 2;     // 16 KB per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;  // 32 KB
 constexpr int kLoadsPerStage = 8;               // per thread: 4 for A, 4 for B
+// Loads still in flight when stage s is needed: the later full stages, plus
+// the A half of the newest one (prologue: the later full stages only).
+constexpr int kVmcntLoop = kLoadsPerStage * (NSTAGE - 3) + kLoadsPerStage / 2;
+constexpr int kVmcntPrologue = kLoadsPerStage * (NSTAGE - 2);
 constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
 constexpr unsigned kMaxRecords = 0x7fffffffu;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
@@ -109,19 +123,23 @@ struct OpK {
       fa[h] = unsigned(r * 64 + 16 * (c ^ swz_k(r)));
     }
   }
+  __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
+                                            int64_t kend) const {
+    const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
+    const unsigned v = (k0 + kc[i] < kend) ? voff[i] : kOOB;
+    load_lds16(r, stage + (wave * 4 + i) * 1024, v);
+  }
   __device__ __forceinline__ void issue(LDS_AS char *stage, int wave, int64_t k0,
                                         int64_t kend) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned v = (k0 + kc[i] < kend) ? voff[i] : kOOB;
-      load_lds16(r, stage + (wave * 4 + i) * 1024, v);
-    }
+    for (int i = 0; i < 4; ++i) issue_one(stage, wave, i, k0, kend);
   }
-  // Fragment of block i (rows wr + 32 i ...), half-step h.
-  __device__ __forceinline__ bf16x8 frag(const LDS_AS char *stage, int i, int h) const {
-    const u32x4 v = *reinterpret_cast<const LDS_AS u32x4 *>(stage + fa[h] + i * 2048);
-    return __builtin_bit_cast(bf16x8, v);
+  static constexpr int kReads = 4;  // LDS reads per half-step
+  // Read number x (0..3) of a half-step: block x (rows wr + 32 x ...).
+  __device__ __forceinline__ void read(bf16x8 (&f)[4], const LDS_AS char *stage, int x,
+                                       int h) const {
+    const LDS_AS char *b = stage + fa[h] + x * 2048;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(f[x]) : "v"(b));
   }
 };
 
@@ -154,25 +172,34 @@ struct OpMN {
       fb[i] = unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
     }
   }
+  __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
+                                            int64_t kend) const {
+    const __amdgpu_buffer_rsrc_t r = rsrc(p + k0 * ld + col0, ((kend - k0) * ld - col0) * 2);
+    load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
+  }
   __device__ __forceinline__ void issue(LDS_AS char *stage, int wave, int64_t k0,
                                         int64_t kend) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc(p + k0 * ld + col0, ((kend - k0) * ld - col0) * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
+    for (int i = 0; i < 4; ++i) issue_one(stage, wave, i, k0, kend);
   }
-  // The transposing reads are issued as inline assembly: issued through the
-  // builtin, the compiler cannot tell them apart from the in-flight LDS-DMA
-  // stage loads and drains the whole load queue (vmcnt(0)) before each one.
-  // Their results are therefore not tracked by the compiler: every consumer
-  // first passes the fragment through lds_wait() below.
-  __device__ __forceinline__ bf16x8 frag(const LDS_AS char *stage, int i, int h) const {
-    // half-step h covers K-rows 16 h ...; the two reads cover K +0..3 and +4..7
-    const LDS_AS char *b = stage + fb[i] + h * 16 * 512;
-    i16x4 lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(b));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(b));
-    const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+  static constexpr int kReads = 8;  // LDS reads per half-step
+  // Read number x (0..7) of a half-step: block x / 2, K-values 4 (x % 2) .. + 3
+  // of each lane's eight (the two halves of the MFMA operand).
+  __device__ __forceinline__ void read(bf16x8 (&f)[4], const LDS_AS char *stage, int x,
+                                       int h) const {
+    const int i = x >> 1;
+    const LDS_AS char *b = stage + fb[i] + h * 16 * 512 + (x & 1) * 4 * 512;
+    i16x4 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(b));
+    auto w = __builtin_bit_cast(i16x8, f[i]);
+    if (x & 1) {
+      w = __builtin_shufflevector(w, __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1),
+                                  0, 1, 2, 3, 8, 9, 10, 11);
+    } else {
+      w = __builtin_shufflevector(w, __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1),
+                                  8, 9, 10, 11, 4, 5, 6, 7);
+    }
+    f[i] = __builtin_bit_cast(bf16x8, w);
   }
 };
 
@@ -184,15 +211,23 @@ struct GemmDesc {
   int64_t M, N, K;
   int64_t split_len;  // K per split
   int tiles_m, tiles_n, splits;
-  int group;          // tile-rows per group of the tile order
+  int group;          // tile-rows (or tile-columns) per group of the tile order
+  int n_first;        // 1: groups of tile-columns, N fastest inside a group
+  int xcd_remap;      // 1: give each XCD a contiguous run of the tile order
 };
 
-// Logits epilogue: S = (acc + b[n]) * inv_tau, fp32.
+// Logits epilogue: S = (acc + b[n]) * inv_tau, fp32, plus the row statistics
+// of each 128-column half-tile: max and sum of exp(S - max) over its columns
+// below N, written as stats[m * n_stat + n / 128] (when stats is given).
 struct EpiLogits {
+  static constexpr bool kRowStats = true;
+  static constexpr bool kReadModifyWrite = false;
   float *S;
   int64_t lds;
   const unsigned short *bias;
   float inv_tau;
+  float2 *stats;
+  int64_t n_stat;
   __device__ __forceinline__ float col_bias(int64_t n) const {
     return bias ? __uint_as_float(unsigned(bias[n]) << 16) : 0.0f;
   }
@@ -210,6 +245,8 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
 
 // dX epilogue: bf16 store when unsplit, fp32 partial per split otherwise.
 struct EpiDx {
+  static constexpr bool kRowStats = false;
+  static constexpr bool kReadModifyWrite = false;
   unsigned short *out;
   int64_t ldo;
   float *partial;
@@ -225,6 +262,8 @@ struct EpiDx {
 
 // dW epilogue: fp32 store or read-modify-write (tiles own disjoint rows).
 struct EpiDw {
+  static constexpr bool kRowStats = false;
+  static constexpr bool kReadModifyWrite = true;
   float *dW;
   int64_t ld;
   int accumulate;
@@ -235,36 +274,52 @@ struct EpiDw {
   }
 };
 
-// Wait for every outstanding LDS read and tie the fragments to the wait, so
-// no MFMA that consumes them can be scheduled above it.
-__device__ __forceinline__ void lds_wait(bf16x8 (&f)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+// The inner loop's MFMAs and LDS fragment reads are volatile inline assembly,
+// so they issue in exactly the order written: each half-step interleaves the
+// reads of the next half-step's fragments and a quarter of the next stage's
+// loads with its 16 MFMAs. The compiler neither sees the reads' latency nor
+// treats the asm as MFMAs, so the LDS waits are explicit and the accumulators
+// rest a few cycles before the epilogue reads them.
+__device__ __forceinline__ void mfma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) {
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];  // 128 KB
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
   LDS_AS char *lds = (LDS_AS char *)smem;
 
-  // ---- tile: XCD-aware remap, then grouped order ----
+  // ---- tile: optional XCD remap, then grouped order ----
   const int T = gridDim.x;
   const int b = blockIdx.x;
-  const int xcd = b & 7, j = b >> 3;
-  const int per = T >> 3, rem = T & 7;
-  const int tl = xcd * per + (xcd < rem ? xcd : rem) + j;
+  int tl = b;
+  if (d.xcd_remap) {
+    const int xcd = b & 7, j = b >> 3;
+    const int per = T >> 3, rem = T & 7;
+    tl = xcd * per + (xcd < rem ? xcd : rem) + j;
+  }
   const int tiles_mn = d.tiles_m * d.tiles_n;
   const int split = tl / tiles_mn;
   const int tmn = tl - split * tiles_mn;
-  const int gsz = d.group * d.tiles_n;
-  const int grp = tmn / gsz;
-  const int first_m = grp * d.group;
-  const int gm = min(d.group, d.tiles_m - first_m);
-  const int local = tmn - grp * gsz;
-  const int tm = first_m + local % gm;
-  const int tn = local / gm;
+  int tm, tn;
+  if (d.n_first) {
+    const int gsz = d.group * d.tiles_m;
+    const int grp = tmn / gsz;
+    const int first = grp * d.group;
+    const int gn = min(d.group, d.tiles_n - first);
+    const int local = tmn - grp * gsz;
+    tn = first + local % gn;
+    tm = local / gn;
+  } else {
+    const int gsz = d.group * d.tiles_n;
+    const int grp = tmn / gsz;
+    const int first = grp * d.group;
+    const int gm = min(d.group, d.tiles_m - first);
+    const int local = tmn - grp * gsz;
+    tm = first + local % gm;
+    tn = local / gm;
+  }
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t kbeg = int64_t(split) * d.split_len;
   const int64_t kend = min(d.K, kbeg + d.split_len);
@@ -273,8 +328,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  typename std::conditional<A_K, OpK, OpMN>::type opa;
-  typename std::conditional<B_K, OpK, OpMN>::type opb;
+  using OA = typename std::conditional<A_K, OpK, OpMN>::type;
+  using OB = typename std::conditional<B_K, OpK, OpMN>::type;
+  OA opa;
+  OB opb;
   if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, wave, lane, wm * 128);
   else opa.init(d.A, d.lda, m0, wave, lane, wm * 128);
   if constexpr (B_K) opb.init(d.B, d.ldb, n0, d.N, wave, lane, wn * 128);
@@ -288,8 +345,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][k][e] = 0.0f;
 
-  // LDS reads per half-step: one per K-contiguous block, two per MN block
-  constexpr int kReadsPerHalf = (A_K ? 4 : 8) + (B_K ? 4 : 8);
   const int nkt = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
   auto stageA = [&](int s) { return lds + (s % NSTAGE) * kStageBytes; };
   auto stageB = [&](int s) { return lds + (s % NSTAGE) * kStageBytes + kOperandBytes; };
@@ -303,94 +358,140 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     // prologue: three stages in flight, wait for the first
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s) issue(s);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntPrologue) : "memory");
     __builtin_amdgcn_s_barrier();
   }
 
   bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[0][i] = fa[1][i] = bf16x8{};
+    fb[0][i] = fb[1][i] = bf16x8{};
+  }
   if (nkt > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[0][i] = opa.frag(stageA(0), i, 0);
-      fb[0][i] = opb.frag(stageB(0), i, 0);
-    }
+    for (int x = 0; x < OA::kReads; ++x) opa.read(fa[0], stageA(0), x, 0);
+#pragma unroll
+    for (int x = 0; x < OB::kReads; ++x) opb.read(fb[0], stageB(0), x, 0);
   }
+
+  // One half-step: 16 MFMAs on (ca, cb); between them the reads of (na, nb)
+  // from the given stages and, after MFMAs 0, 4, 8, 12, one stage load each.
+  auto half = [&](bf16x8 (&ca)[4], bf16x8 (&cb)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
+                  const LDS_AS char *sa, const LDS_AS char *sb, int h, auto &&load) {
+    constexpr int ea = 16 / OA::kReads, eb = 16 / OB::kReads;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      mfma(acc[x >> 2][x & 3], ca[x >> 2], cb[x & 3]);
+      if (x % ea == 0) opa.read(na, sa, x / ea, h);
+      if (x % eb == eb / 2) opb.read(nb, sb, x / eb, h);
+      if ((x & 3) == 0) load(x >> 2);
+    }
+  };
 
   for (int kt = 0; kt < nkt; ++kt) {
-    // Fragments of half-step 0 (read during the previous half-step) are ready.
-    lds_wait(fa[0]);
-    lds_wait(fb[0]);
-    // [B] half-step 0 MFMAs; meanwhile request the A slice of stage kt + 3
-    // (past the end: zero-filled, never read) and read the half-step 1
-    // fragments of stage kt.
-    {
-      const int64_t k0 = kbeg + int64_t(kt + NSTAGE - 1) * BK;
-      opa.issue(stageA(kt + NSTAGE - 1), wave, k0, kend);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[1][i] = opa.frag(stageA(kt), i, 1);
-      fb[1][i] = opb.frag(stageB(kt), i, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][k], acc[i][k], 0, 0, 0);
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      if ((x & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    }
-
+    const int64_t k_next = kbeg + int64_t(kt + NSTAGE - 1) * BK;
+    // [B] half-step 0 of stage kt; read half-step 1 of stage kt; request the
+    // A slice of stage kt + NSTAGE - 1 (past the end: zero-filled, unread).
+    wait_lds();
+    half(fa[0], fb[0], fa[1], fb[1], stageA(kt), stageB(kt), 1,
+         [&](int q) { opa.issue_one(stageA(kt + NSTAGE - 1), wave, q, k_next, kend); });
     // [C] stage kt + 1 complete in LDS for every wave: of the loads issued so
-    // far only stage kt + 2 (8 per thread) and the A half of stage kt + 3 (4)
-    // may still be in flight.
-    lds_wait(fa[1]);
-    lds_wait(fb[1]);
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    // far only the later stages (8 per thread each) and the A half of stage
+    // kt + NSTAGE - 1 (4) may still be in flight.
+    wait_lds();
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntLoop) : "memory");
     __builtin_amdgcn_s_barrier();
-
-    // [D] half-step 1 MFMAs; request the B slice of stage kt + 3 and read the
-    // half-step 0 fragments of stage kt + 1.
-    {
-      const int64_t k0 = kbeg + int64_t(kt + NSTAGE - 1) * BK;
-      opb.issue(stageB(kt + NSTAGE - 1), wave, k0, kend);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[0][i] = opa.frag(stageA(kt + 1), i, 0);
-      fb[0][i] = opb.frag(stageB(kt + 1), i, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][k], acc[i][k], 0, 0, 0);
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      if ((x & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    }
+    // [D] half-step 1 of stage kt; read half-step 0 of stage kt + 1; request
+    // the B slice of stage kt + NSTAGE - 1.
+    half(fa[1], fb[1], fa[0], fb[0], stageA(kt + 1), stageB(kt + 1), 0,
+         [&](int q) { opb.issue_one(stageB(kt + NSTAGE - 1), wave, q, k_next, kend); });
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // Accumulator layout of the 32 x 32 block: lane l holds column l % 32;
   // register r holds row 8 (r / 4) + 4 (l / 32) + r % 4.
   const int fhalf = lane >> 5;
+  if constexpr (Epi::kRowStats) {
+    // One output row of this wave's 128 columns lives in 32 lanes (the lanes
+    // of one half-wave) x 4 blocks: reduce in registers, then across the 32
+    // lanes with xor-shuffles that stay inside the half-wave.
+    const int64_t nh = n0 + wn * 128;  // first column of this half-tile
+    float bn[4];
+    bool okn[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t n = n0 + wn * 128 + k * 32 + (lane & 31);
-    if (n >= d.N) continue;
-    const float bn = epi.col_bias(n);
+    for (int k = 0; k < 4; ++k) {
+      const int64_t n = nh + k * 32 + (lane & 31);
+      okn[k] = n < d.N;
+      bn[k] = okn[k] ? epi.col_bias(n) : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
-        if (m < d.M) epi.put(m, n, acc[i][k][r], bn, split);
+        float v[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = (acc[i][k][r] + bn[k]) * epi.inv_tau;
+          if (okn[k]) {
+            if (m < d.M) epi.S[m * epi.lds + nh + k * 32 + (lane & 31)] = v[k];
+            mx = fmaxf(mx, v[k]);
+          }
+        }
+        if (epi.stats) {
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          float se = 0.0f;
+          if (mx != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (okn[k]) se += __expf(v[k] - mx);
+          }
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+          if ((lane & 31) == 0 && m < d.M && nh < d.N)
+            epi.stats[m * epi.n_stat + (nh >> 7)] = make_float2(mx, se);
+        }
+      }
+    }
+  } else if constexpr (Epi::kReadModifyWrite) {
+    // Accumulating store: each 32 x 32 block's 16 old values per lane are
+    // loaded together before any of them is written back, so the loads of a
+    // block are in flight at once instead of one round trip per element.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t n = n0 + wn * 128 + k * 32 + (lane & 31);
+      if (n >= d.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
+          old[r] = (epi.accumulate && m < d.M) ? epi.dW[m * epi.ld + n] : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
+          if (m < d.M) epi.dW[m * epi.ld + n] = old[r] + acc[i][k][r];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t n = n0 + wn * 128 + k * 32 + (lane & 31);
+      if (n >= d.N) continue;
+      const float bn = epi.col_bias(n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
+          if (m < d.M) epi.put(m, n, acc[i][k][r], bn, split);
+        }
       }
     }
   }
@@ -412,8 +513,8 @@ void launch(const GemmDesc &d0, const Epi &epi, hipStream_t st) {
 }  // namespace
 
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
-                        const void *b, float inv_tau, float *S, int64_t lds, int64_t M,
-                        int64_t N, int64_t K, hipStream_t st) {
+                        const void *b, float inv_tau, float *S, int64_t lds, float2 *stats,
+                        int64_t n_stat, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   GemmDesc d{};
   d.A = static_cast<const unsigned short *>(X);
   d.lda = ldx;
@@ -424,8 +525,10 @@ void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
   d.K = K;
   d.split_len = K;
   d.splits = 1;
-  d.group = 8;
-  EpiLogits e{S, lds, static_cast<const unsigned short *>(b), inv_tau};
+  d.group = 16;       // measured best for the head shapes: see the tile-order note
+  d.n_first = 0;
+  d.xcd_remap = 0;
+  EpiLogits e{S, lds, static_cast<const unsigned short *>(b), inv_tau, stats, n_stat};
   launch<true, true>(d, e, st);
 }
 
@@ -442,7 +545,9 @@ void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw, voi
   d.K = K;
   d.split_len = splits > 1 ? split_len : K;
   d.splits = int(splits);
-  d.group = 8;
+  d.group = 4;
+  d.n_first = 1;
+  d.xcd_remap = 0;
   EpiDx e{static_cast<unsigned short *>(dX), ldo, splits > 1 ? partial : nullptr, M, N};
   launch<true, false>(d, e, st);
 }
@@ -459,7 +564,9 @@ void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx, flo
   d.K = K;
   d.split_len = K;
   d.splits = 1;
-  d.group = 4;
+  d.group = 8;
+  d.n_first = 0;
+  d.xcd_remap = 1;
   EpiDw e{dW, N, accumulate};
   launch<false, false>(d, e, st);
 }

@@ -78,6 +78,18 @@ __device__ __forceinline__ Load4 load_group(const float *row, int64_t g, int64_t
   return r;
 }
 
+// Block-wide reduction helpers: wave shuffles, then the four waves' partials
+// combined in a fixed order by thread 0 through LDS.
+__device__ __forceinline__ float block_sum(float v, float (*red)[8], int slot, int lane,
+                                           int wave) {
+  v = wave_sum(v);
+  if (lane == 0) red[wave][slot] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int w = 0; w < kRowWaves; ++w) t += red[w][slot];
+  return t;
+}
+
 template <int HEAD>
 __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   __shared__ float red[kRowWaves][8];
@@ -119,38 +131,60 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   const bool q_vec = HEAD == HEAD_KL && (V % 4 == 0) &&
                      ((reinterpret_cast<uintptr_t>(a.target) & 15) == 0);
 
-  // ---- pass 1: max, sum exp, and the KL sums ----
+  // ---- statistics: max and sum exp (from the GEMM's block statistics, or a
+  // pass over the logits), and for KL sum q, sum q log max(q, eps) ----
   float m = -INFINITY, s = 0.0f;
   float sq = 0.0f, sqlogq = 0.0f, sqx = 0.0f;
-  for (int64_t g = tid; g < ngroups; g += kRowThreads) {
-    Load4 x = load_group(Srow, g, V, true);
-    const int64_t e = 4 * g;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (e + i < V) mx = fmaxf(mx, x.v[i]);
-    if (mx > m) {
-      s *= __expf(m - mx);
-      m = mx;
+  if (a.stats) {
+    const float2 *st = a.stats + lr * a.n_stat;
+    for (int64_t t = tid; t < a.n_stat; t += kRowThreads) {
+      const float2 p = st[t];
+      lse_merge(m, s, p.x, p.y);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (e + i < V) s += __expf(x.v[i] - m);
     if (HEAD == HEAD_KL) {
-      Load4 t = load_group(q, g, V, q_vec);
+      for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+        Load4 t = load_group(q, g, V, q_vec);
+        const int64_t e = 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (e + i < V) {
-          const float qi = t.v[i];
-          sq += qi;
-          sqlogq += qi * __logf(fmaxf(qi, a.eps));
-          sqx += qi * x.v[i];
+        for (int i = 0; i < 4; ++i) {
+          if (e + i < V) {
+            sq += t.v[i];
+            sqlogq += t.v[i] * __logf(fmaxf(t.v[i], a.eps));
+          }
+        }
+      }
+    }
+  } else {
+    for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+      Load4 x = load_group(Srow, g, V, true);
+      const int64_t e = 4 * g;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e + i < V) mx = fmaxf(mx, x.v[i]);
+      if (mx > m) {
+        s *= __expf(m - mx);
+        m = mx;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e + i < V) s += __expf(x.v[i] - m);
+      if (HEAD == HEAD_KL) {
+        Load4 t = load_group(q, g, V, q_vec);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (e + i < V) {
+            const float qi = t.v[i];
+            sq += qi;
+            sqlogq += qi * __logf(fmaxf(qi, a.eps));
+            sqx += qi * x.v[i];
+          }
         }
       }
     }
   }
   float s_label = 0.0f;
-  if (HEAD == HEAD_SEL && tid == 0) s_label = Srow[y];
+  if (HEAD == HEAD_SEL && tid == 0) s_label = Srow[y];  // read before any write
 
   // wave reduction, then across waves in a fixed order
   {
@@ -182,14 +216,11 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
         B += red[w][4];
       }
     const float l = M + __logf(Ssum);
-    float rv;
-    if (HEAD == HEAD_KL)
-      rv = A - B + Q * l;  // sum_v q log q - q (S - l)
-    else
-      rv = s_label - l;    // log p(y)
-    a.rowval[gr] = rv;
+    if (HEAD == HEAD_SEL) a.rowval[gr] = s_label - l;  // log p(y)
+    else if (!a.stats) a.rowval[gr] = A - B + Q * l;   // sum_v q log q - q (S - l)
     bcast[0] = l;
     bcast[1] = Q;
+    bcast[2] = A;
   }
   __syncthreads();
   const float l = bcast[0];
@@ -204,10 +235,11 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     coef = g * w * a.inv_tau;
   }
 
-  // ---- pass 2: dZ = dS / tau, written in place ----
+  // ---- dZ = dS / tau, written in place ----
   // The bf16 dZ of element v goes to bytes [2v, 2v + 2) of the row, i.e. over
   // float slots that an earlier strip (or this strip, before the barrier)
   // has already read. Each strip's loads complete before its barrier.
+  float bq = 0.0f;  // KL with block statistics: sum q S, accumulated here
   for (int64_t base = 0; base < ngroups; base += kStrip) {
     Load4 xs[kUnroll];
     Load4 qs[kUnroll];
@@ -229,10 +261,12 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = __expf(xs[u].v[i] - l);
-        if (HEAD == HEAD_KL)
+        if (HEAD == HEAD_KL) {
           d[i] = coef * (Qr * p - qs[u].v[i]);
-        else
+          if (e + i < V) bq += qs[u].v[i] * xs[u].v[i];
+        } else {
           d[i] = coef * (((e + i) == y ? 1.0f : 0.0f) - p);
+        }
       }
       if (a.dz_bf16) {
         if (e + 4 <= V) {
@@ -253,6 +287,10 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
         }
       }
     }
+  }
+  if (HEAD == HEAD_KL && a.stats) {
+    const float B = block_sum(bq, red, 5, lane, wave);
+    if (tid == 0) a.rowval[gr] = bcast[2] - B + Qr * l;
   }
   // Every read of this row finished before the last strip's barrier.
   if (a.dz_bf16) zero_pad(Zb, V, tid);
