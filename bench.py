@@ -32,6 +32,25 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "fwd+bwd tokens/sec at H=4096,V=128256 bf16; % of bf16 MFMA peak"
+COPY_BYTES = 1 << 30
+
+
+def measured_traffic(case, kind):
+    """HBM bytes per launch of `kind` from the committed counter summary of
+    this workload, or None if there is none or the kernels changed since."""
+    from lm_head_projection_token_amd import profiling
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("src_sha256") != profiling.source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kind)
+    if not k:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
 
 
 def gemm_flops(case):
@@ -47,7 +66,7 @@ def kernel_flops(kind, case):
     return {"logits": per, "dx": per, "dw": per if case.compute_dW else 0.0}.get(kind, 0.0)
 
 
-def cpu_baseline(inp, case, rows_small=32, rows_big=160):
+def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
     """Time the oracle on two row samples and extrapolate to the full batch."""
     import numpy as np
 
@@ -99,7 +118,21 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-rows", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+
+        n = COPY_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fused lm_head loss is a single-GPU "
@@ -173,7 +206,8 @@ def main():
     per_launch = kernel_flops(dom, case) / plan.n_chunks
     achieved = per_launch / (kernels[dom]["avg_ms"] / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": measured_traffic(case, dom),
                 "flops_per_launch": per_launch}
     row = kernels.get("row")
     if row:
