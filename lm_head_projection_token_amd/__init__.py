@@ -90,6 +90,12 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m lm_head_projection_token_amd.build`")
+    # torch ships its own HIP and HSA runtimes. Loading torch first lets
+    # libfll.so's libamdhip64.so.7 dependency resolve to torch's copy (same
+    # soname), so the process holds one runtime; loaded the other way round,
+    # two runtimes end up in one process and the second sees no device.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     lib.fll_plan.argtypes = [ctypes.POINTER(FllProblem), ctypes.c_size_t, ctypes.c_int64,
                              ctypes.POINTER(FllPlan)]

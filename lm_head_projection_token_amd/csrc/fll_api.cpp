@@ -253,6 +253,10 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   int st = check_args(plan, args);
   if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // hipGetLastError reports the last failure of any HIP caller on this
+  // thread; drop a stale one left by another library so only this call's
+  // launches are judged below.
+  (void)hipGetLastError();
   const fll_problem &p = plan->p;
   const fll_args &a = *args;
   char *ws = static_cast<char *>(a.workspace);

@@ -240,3 +240,18 @@ def test_strerror_covers_every_status():
     for s in (0, -1, -2, -3, -4):
         assert fll.fll_strerror(s) and fll.fll_strerror(s) != "unknown status"
     assert fll.fll_strerror(42) == "unknown status"
+
+
+def test_one_hip_runtime_in_the_process():
+    # torch bundles its own HIP runtime; the package must load torch before
+    # libfll.so so that both use one runtime (two in one process leave the
+    # second without a device).
+    code = (
+        "import lm_head_projection_token_amd, torch\n"
+        "maps = open('/proc/self/maps').read().split('\\n')\n"
+        "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+        "print(len(libs)); print(sorted(libs))\n"
+    )
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True,
+                         cwd=ROOT, check=True).stdout.split("\n")
+    assert out[0] == "1", out
