@@ -231,9 +231,6 @@ struct EpiLogits {
   __device__ __forceinline__ float col_bias(int64_t n) const {
     return bias ? __uint_as_float(unsigned(bias[n]) << 16) : 0.0f;
   }
-  __device__ __forceinline__ void put(int64_t m, int64_t n, float v, float bn, int) const {
-    S[m * lds + n] = (v + bn) * inv_tau;
-  }
 };
 
 __device__ __forceinline__ unsigned short f2bf(float f) {
@@ -244,6 +241,7 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
 }
 
 // dX epilogue: bf16 store when unsplit, fp32 partial per split otherwise.
+// Stores four consecutive columns n .. n + 3 of row m (n is a multiple of 4).
 struct EpiDx {
   static constexpr bool kRowStats = false;
   static constexpr bool kReadModifyWrite = false;
@@ -251,26 +249,60 @@ struct EpiDx {
   int64_t ldo;
   float *partial;
   int64_t M, N;
-  __device__ __forceinline__ float col_bias(int64_t) const { return 0.0f; }
-  __device__ __forceinline__ void put(int64_t m, int64_t n, float v, float, int split) const {
-    if (partial)
-      partial[(int64_t(split) * M + m) * N + n] = v;
-    else
-      out[m * ldo + n] = f2bf(v);
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,
+                                         int split) const {
+    const float ve[4] = {v.x, v.y, v.z, v.w};
+    if (partial) {
+      float *p = partial + (int64_t(split) * M + m) * N + n;
+      if (n + 4 <= nmax) {
+        *reinterpret_cast<float4 *>(p) = v;
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (n + e < nmax) p[e] = ve[e];
+      }
+    } else {
+      unsigned short *p = out + m * ldo + n;
+      if (n + 4 <= nmax) {
+        uint2 pk;
+        pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
+        pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+        *reinterpret_cast<uint2 *>(p) = pk;
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (n + e < nmax) p[e] = f2bf(ve[e]);
+      }
+    }
   }
 };
 
-// dW epilogue: fp32 store or read-modify-write (tiles own disjoint rows).
+// dW epilogue: fp32 store, or read-modify-write across token chunks (each
+// tile owns its rows, so there are no atomics).
 struct EpiDw {
   static constexpr bool kRowStats = false;
   static constexpr bool kReadModifyWrite = true;
   float *dW;
   int64_t ld;
   int accumulate;
-  __device__ __forceinline__ float col_bias(int64_t) const { return 0.0f; }
-  __device__ __forceinline__ void put(int64_t m, int64_t n, float v, float, int) const {
+  __device__ __forceinline__ float4 load4(int64_t m, int64_t n, int64_t nmax) const {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!accumulate) return v;
+    const float *p = dW + m * ld + n;
+    if (n + 4 <= nmax) return *reinterpret_cast<const float4 *>(p);
+    if (n + 0 < nmax) v.x = p[0];
+    if (n + 1 < nmax) v.y = p[1];
+    if (n + 2 < nmax) v.z = p[2];
+    return v;
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,
+                                         int) const {
     float *p = dW + m * ld + n;
-    *p = accumulate ? *p + v : v;
+    if (n + 4 <= nmax) {
+      *reinterpret_cast<float4 *>(p) = v;
+    } else {
+      const float ve[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 4; ++e)
+        if (n + e < nmax) p[e] = ve[e];
+    }
   }
 };
 
@@ -382,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     constexpr int ea = 16 / OA::kReads, eb = 16 / OB::kReads;
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      mfma(acc[x >> 2][x & 3], ca[x >> 2], cb[x & 3]);
+      mfma(acc[x >> 2][x & 3], cb[x & 3], ca[x >> 2]);
       if (x % ea == 0) opa.read(na, sa, x / ea, h);
       if (x % eb == eb / 2) opb.read(nb, sb, x / eb, h);
       if ((x & 3) == 0) load(x >> 2);
@@ -409,88 +441,108 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  // Accumulator layout of the 32 x 32 block: lane l holds column l % 32;
-  // register r holds row 8 (r / 4) + 4 (l / 32) + r % 4.
-  const int fhalf = lane >> 5;
+  // The MFMAs take the B fragment as their first operand, so each 32 x 32
+  // accumulator block holds the transposed product: lane l owns output row
+  // m = l % 32 of the block, and register r holds column
+  // 8 (r / 4) + 4 (l / 32) + r % 4. A lane therefore owns, for each of its
+  // four rows, 64 of the wave's 128 columns in runs of four (16-byte
+  // stores), and lane l ^ 32 owns the other 64.
+  const int lrow = lane & 31;
+  const int lcol = 4 * (lane >> 5);
   if constexpr (Epi::kRowStats) {
-    // One output row of this wave's 128 columns lives in 32 lanes (the lanes
-    // of one half-wave) x 4 blocks: reduce in registers, then across the 32
-    // lanes with xor-shuffles that stay inside the half-wave.
-    const int64_t nh = n0 + wn * 128;  // first column of this half-tile
-    float bn[4];
-    bool okn[4];
+    const int64_t nh = n0 + wn * 128;  // first column of this 128-column half-tile
+    float bias[4][4][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t n = nh + k * 32 + (lane & 31);
-      okn[k] = n < d.N;
-      bn[k] = okn[k] ? epi.col_bias(n) : 0.0f;
-    }
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t n = nh + k * 32 + 8 * q + lcol + e;
+          bias[k][q][e] = n < d.N ? epi.col_bias(n) : 0.0f;
+        }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + lrow;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
-        float v[4];
-        float mx = -INFINITY;
+      for (int k = 0; k < 4; ++k) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[k] = (acc[i][k][r] + bn[k]) * epi.inv_tau;
-          if (okn[k]) {
-            if (m < d.M) epi.S[m * epi.lds + nh + k * 32 + (lane & 31)] = v[k];
-            mx = fmaxf(mx, v[k]);
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = nh + k * 32 + 8 * q + lcol;
+          float4 v;
+          v.x = (acc[i][k][4 * q + 0] + bias[k][q][0]) * epi.inv_tau;
+          v.y = (acc[i][k][4 * q + 1] + bias[k][q][1]) * epi.inv_tau;
+          v.z = (acc[i][k][4 * q + 2] + bias[k][q][2]) * epi.inv_tau;
+          v.w = (acc[i][k][4 * q + 3] + bias[k][q][3]) * epi.inv_tau;
+          acc[i][k][4 * q + 0] = v.x;
+          acc[i][k][4 * q + 1] = v.y;
+          acc[i][k][4 * q + 2] = v.z;
+          acc[i][k][4 * q + 3] = v.w;
+          float *dst = epi.S + m * epi.lds + n;
+          if (n + 4 <= d.N) {
+            if (m < d.M) *reinterpret_cast<float4 *>(dst) = v;
+            mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+          } else {
+            const float ve[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < d.N) {
+                if (m < d.M) dst[e] = ve[e];
+                mx = fmaxf(mx, ve[e]);
+              }
           }
-        }
-        if (epi.stats) {
-#pragma unroll
-          for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-          float se = 0.0f;
-          if (mx != -INFINITY) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (okn[k]) se += __expf(v[k] - mx);
-          }
-#pragma unroll
-          for (int o = 16; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
-          if ((lane & 31) == 0 && m < d.M && nh < d.N)
-            epi.stats[m * epi.n_stat + (nh >> 7)] = make_float2(mx, se);
         }
       }
-    }
-  } else if constexpr (Epi::kReadModifyWrite) {
-    // Accumulating store: each 32 x 32 block's 16 old values per lane are
-    // loaded together before any of them is written back, so the loads of a
-    // block are in flight at once instead of one round trip per element.
+      if (epi.stats) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float se = 0.0f;
+        if (mx != -INFINITY) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t n = n0 + wn * 128 + k * 32 + (lane & 31);
-      if (n >= d.N) continue;
+          for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float old[16];
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
-          old[r] = (epi.accumulate && m < d.M) ? epi.dW[m * epi.ld + n] : 0.0f;
+              for (int e = 0; e < 4; ++e)
+                if (nh + k * 32 + 8 * q + lcol + e < d.N) se += __expf(acc[i][k][4 * q + e] - mx);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
-          if (m < d.M) epi.dW[m * epi.ld + n] = old[r] + acc[i][k][r];
-        }
+        se += __shfl_xor(se, 32, 64);
+        if (lane < 32 && m < d.M && nh < d.N)
+          epi.stats[m * epi.n_stat + (nh >> 7)] = make_float2(mx, se);
       }
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t n = n0 + wn * 128 + k * 32 + (lane & 31);
-      if (n >= d.N) continue;
-      const float bn = epi.col_bias(n);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + lrow;
+      if (m >= d.M) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (Epi::kReadModifyWrite) {
+          // old values of the block's 16 columns first, all loads in flight
+          float4 old[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fhalf * 4 + (r & 3);
-          if (m < d.M) epi.put(m, n, acc[i][k][r], bn, split);
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 128 + k * 32 + 8 * q + lcol;
+            old[q] = epi.load4(m, n, d.N);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 128 + k * 32 + 8 * q + lcol;
+            const float4 v = make_float4(old[q].x + acc[i][k][4 * q + 0],
+                                         old[q].y + acc[i][k][4 * q + 1],
+                                         old[q].z + acc[i][k][4 * q + 2],
+                                         old[q].w + acc[i][k][4 * q + 3]);
+            epi.store4(m, n, d.N, v, split);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 128 + k * 32 + 8 * q + lcol;
+            const float4 v = make_float4(acc[i][k][4 * q + 0], acc[i][k][4 * q + 1],
+                                         acc[i][k][4 * q + 2], acc[i][k][4 * q + 3]);
+            epi.store4(m, n, d.N, v, split);
+          }
         }
       }
     }
