@@ -17,6 +17,7 @@
  *   FLL_HEAD_SELECTIVE_LOGPROB: L_r = logP_{r, y_r}, weighted by w_r
  *       the per-token selective log-prob of the GRPO family
  *       [frozen lm_head GRPO page, Summary].
+ *   FLL_HEAD_CROSS_ENTROPY:     L_r = -logP_{r, y_r}, weighted by w_r
  *
  * The work runs in token chunks, and each chunk's gradient is formed inside
  * the same call (gradient-in-forward), so the BT x V logits are never
@@ -59,13 +60,21 @@ typedef enum {
   FLL_ERR_HIP = -4          /* a HIP launch or runtime call failed          */
 } fll_status;
 
-typedef enum { FLL_HEAD_KL = 0, FLL_HEAD_SELECTIVE_LOGPROB = 1 } fll_head;
+/* FLL_HEAD_CROSS_ENTROPY: L_r = -log p(y_r), optionally weighted by w_r --
+ * the KL head against a one-hot target, i.e. the fused linear cross-entropy
+ * loss whose chunk geometry the FusedLinearKLDivLoss page (Summary) reuses. */
+typedef enum {
+  FLL_HEAD_KL = 0,
+  FLL_HEAD_SELECTIVE_LOGPROB = 1,
+  FLL_HEAD_CROSS_ENTROPY = 2
+} fll_head;
 
 /* Reductions with the semantics of torch.nn.KLDivLoss
  * [FusedLinearKLDivLoss page, Details]. With n = the number of rows whose
  * label is not ignore_index (all rows when labels is NULL):
  *   BATCHMEAN: g = 1/n;  MEAN: g = 1/(n V) for KL, 1/n for the selective
- *   head (its tokens are the batch);  SUM: g = 1;  n = 0 gives g = 0.
+ *   and cross-entropy heads (their tokens are the batch);  SUM: g = 1;
+ *   n = 0 gives g = 0.
  * NONE is refused with FLL_ERR_UNSUPPORTED: gradient-in-forward needs a
  * scalar loss [FusedLinearKLDivLoss page, Details]. */
 typedef enum {
@@ -119,20 +128,21 @@ typedef struct {
   const void *X;       /* [BT x H], dtype                                     */
   const void *W;       /* [V x H], dtype                                      */
   const void *b;       /* [V], dtype; NULL iff has_bias == 0                  */
-  const int64_t *labels; /* [BT]. SELECTIVE: required, values in [0, V) or
-                            ignore_index. KL: optional row mask (a row is
-                            ignored iff its label == ignore_index).           */
+  const int64_t *labels; /* [BT]. SELECTIVE, CROSS_ENTROPY: required, values
+                            in [0, V) or ignore_index. KL: optional row mask
+                            (a row is ignored iff its label == ignore_index). */
   const float *target; /* KL: [BT x V] fp32 target probabilities, required.
                           Rows of ignored tokens are never read.              */
-  const float *weights; /* SELECTIVE: [BT] fp32 per-token weights (advantages);
-                           NULL means all 1.                                  */
+  const float *weights; /* SELECTIVE, CROSS_ENTROPY: [BT] fp32 per-token
+                           weights (advantages); NULL means all 1. KL: NULL.  */
   void *dX;            /* [BT x H], dtype: written (every row, ignored = 0)    */
   float *dW;           /* [V x H] fp32: written iff compute_dW, else untouched
                           and may be NULL                                     */
   float *db;           /* [V] fp32: written iff compute_db, else untouched    */
   float *loss;         /* [1] fp32: written                                   */
-  float *per_row;      /* optional [BT] fp32: KL_r (KL) or log p(y_r)
-                          (SELECTIVE) before weighting; 0 on ignored rows     */
+  float *per_row;      /* optional [BT] fp32: KL_r (KL), log p(y_r)
+                          (SELECTIVE) or -log p(y_r) (CROSS_ENTROPY) before
+                          weighting; 0 on ignored rows                       */
   void *workspace;     /* >= plan.workspace_bytes, 256-byte aligned; contents
                           are scratch and need no initialisation              */
   size_t workspace_bytes;
@@ -168,7 +178,8 @@ int fll_plan(const fll_problem *problem, size_t max_workspace_bytes,
  * dW / db kernels are launched only when compute_dW / compute_db are set
  * [frozen lm_head GRPO page, Summary; LoRA normalization page, Key Changes].
  *
- * A non-ignored SELECTIVE label outside [0, V) is not a memory error: that
+ * A non-ignored label outside [0, V) (SELECTIVE, CROSS_ENTROPY) is not a
+ * memory error: that
  * row's per_row value and the loss become NaN and its dlogits are zero.
  * Calls that share a workspace must be ordered on one stream.
  *

@@ -31,7 +31,9 @@ FLL_ERR_HIP = -4
 
 FLL_HEAD_KL = 0
 FLL_HEAD_SELECTIVE_LOGPROB = 1
-HEADS = {"kl": FLL_HEAD_KL, "selective": FLL_HEAD_SELECTIVE_LOGPROB}
+FLL_HEAD_CROSS_ENTROPY = 2
+HEADS = {"kl": FLL_HEAD_KL, "selective": FLL_HEAD_SELECTIVE_LOGPROB,
+         "ce": FLL_HEAD_CROSS_ENTROPY}
 
 FLL_RED_BATCHMEAN, FLL_RED_MEAN, FLL_RED_SUM, FLL_RED_NONE = 0, 1, 2, 3
 REDUCTIONS = {"batchmean": 0, "mean": 1, "sum": 2, "none": 3}

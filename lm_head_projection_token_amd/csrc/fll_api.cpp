@@ -48,7 +48,8 @@ int check_problem(const fll_problem *p) {
     return fail(FLL_ERR_INVALID_ARG, "unknown reduction %d", p->reduction);
   if (p->dtype != FLL_BF16 && p->dtype != FLL_FP32)
     return fail(FLL_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-  if (p->head != FLL_HEAD_KL && p->head != FLL_HEAD_SELECTIVE_LOGPROB)
+  if (p->head != FLL_HEAD_KL && p->head != FLL_HEAD_SELECTIVE_LOGPROB &&
+      p->head != FLL_HEAD_CROSS_ENTROPY)
     return fail(FLL_ERR_INVALID_ARG, "unknown head %d", p->head);
   if (p->BT < 0) return fail(FLL_ERR_INVALID_ARG, "BT < 0");
   if (p->V < 1) return fail(FLL_ERR_INVALID_ARG, "V must be >= 1");
@@ -160,9 +161,11 @@ int check_args(const fll_plan_t *pl, const fll_args *a) {
   if (!a->X || !a->W || !a->dX) return fail(FLL_ERR_INVALID_ARG, "X, W and dX are required");
   if (!aligned(a->X, 16) || !aligned(a->W, 16) || !aligned(a->dX, 16))
     return fail(FLL_ERR_INVALID_ARG, "X, W and dX must be 16-byte aligned");
-  if (p.head == FLL_HEAD_SELECTIVE_LOGPROB) {
-    if (!a->labels) return fail(FLL_ERR_INVALID_ARG, "the selective head needs labels");
-    if (a->target) return fail(FLL_ERR_INVALID_ARG, "target given for the selective head");
+  if (p.head != FLL_HEAD_KL) {
+    if (!a->labels)
+      return fail(FLL_ERR_INVALID_ARG, "the selective and cross-entropy heads need labels");
+    if (a->target)
+      return fail(FLL_ERR_INVALID_ARG, "target given for a label head");
   } else {
     if (!a->target) return fail(FLL_ERR_INVALID_ARG, "the KL head needs a target");
     if (a->weights) return fail(FLL_ERR_INVALID_ARG, "weights given for the KL head");
@@ -359,8 +362,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   }
   {
     Probe pr(FLL_K_FINAL, s);
-    fll::launch_finalize(rowval, p.head == FLL_HEAD_SELECTIVE_LOGPROB ? a.weights : nullptr,
-                         p.BT, sc, a.loss, s);
+    fll::launch_finalize(rowval, p.head != FLL_HEAD_KL ? a.weights : nullptr, p.BT, sc,
+                         a.loss, s);
   }
   return hip_check("loss reduction");
 }

@@ -18,11 +18,12 @@ namespace {
 
 constexpr int kRowThreads = 256;
 constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kUnroll = 4;  // float4 groups per thread per strip
+constexpr int kUnroll = 8;  // float4 groups per thread per strip
 constexpr int kStrip = kRowThreads * kUnroll;  // float4 groups per strip
 
 constexpr int HEAD_KL = 0;
 constexpr int HEAD_SEL = 1;
+constexpr int HEAD_CE = 2;  // the selective head with the opposite sign
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     y = a.labels[gr];
     valid = (y != a.ignore_index);
   }
-  const bool bad_label = HEAD == HEAD_SEL && valid && (y < 0 || y >= V);
+  const bool bad_label = HEAD != HEAD_KL && valid && (y < 0 || y >= V);
   if (!valid || bad_label) {
     // The row takes no part: its dlogits are zero.
     for (int64_t g = tid; g < ngroups; g += kRowThreads) {
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     }
   }
   float s_label = 0.0f;
-  if (HEAD == HEAD_SEL && tid == 0) s_label = Srow[y];  // read before any write
+  if (HEAD != HEAD_KL && tid == 0) s_label = Srow[y];  // read before any write
 
   // wave reduction, then across waves in a fixed order
   {
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
       }
     const float l = M + __logf(Ssum);
     if (HEAD == HEAD_SEL) a.rowval[gr] = s_label - l;  // log p(y)
+    if (HEAD == HEAD_CE) a.rowval[gr] = l - s_label;   // -log p(y)
     else if (!a.stats) a.rowval[gr] = A - B + Q * l;   // sum_v q log q - q (S - l)
     bcast[0] = l;
     bcast[1] = Q;
@@ -231,8 +233,9 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     coef = g * a.inv_tau;
     Qr = bcast[1];
   } else {
+    // selective: dS = g w (onehot - p); cross-entropy: dS = g w (p - onehot)
     const float w = a.weights ? a.weights[gr] : 1.0f;
-    coef = g * w * a.inv_tau;
+    coef = (HEAD == HEAD_CE ? -g : g) * w * a.inv_tau;
   }
 
   // ---- dZ = dS / tau, written in place ----
@@ -422,8 +425,10 @@ void launch_row(const RowArgs &a, hipStream_t st) {
   if (a.rows <= 0) return;
   if (a.head == HEAD_KL)
     hipLaunchKernelGGL(row_kernel<HEAD_KL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
-  else
+  else if (a.head == HEAD_SEL)
     hipLaunchKernelGGL(row_kernel<HEAD_SEL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(row_kernel<HEAD_CE>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
 }
 
 void launch_colsum(const void *dZ, int dz_bf16, int64_t ldz, int64_t rows, int64_t V,

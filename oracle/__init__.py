@@ -1,8 +1,10 @@
 """CPU float64 oracle (test infrastructure only; see ``fll_oracle``)."""
 
 from .fll_oracle import (  # noqa: F401
+    HEAD_CE,
     HEAD_KL,
     HEAD_SELECTIVE,
+    ce_rows,
     dlogits,
     fwd_bwd,
     kl_rows,

@@ -22,9 +22,10 @@ W [V, H] (+ b [V]):
 
 1. logits Z = X W^T + b, tempered S = Z / tau (model side only).
 2. log-softmax over the vocabulary: logP = S - lse(S).
-3. the per-row term of one of two heads:
+3. the per-row term of one of three heads:
    KL:        L_r = sum_v q_rv * log(max(q_rv, eps)) - q_rv * logP_rv
    SELECTIVE: L_r = logP_{r, y_r}   (weighted by the advantage w_r)
+   CE:        L_r = -logP_{r, y_r}  (cross-entropy: KL against a one-hot target)
 4. loss = g * sum_r w_r L_r with g from the reduction and the count of rows
    whose label is not ``ignore_index``.
 5. the exact gradient: dS = d loss / d S, dZ = dS / tau, then
@@ -50,6 +51,7 @@ import numpy as np
 
 HEAD_KL = "kl"
 HEAD_SELECTIVE = "selective"
+HEAD_CE = "ce"
 REDUCTIONS = ("batchmean", "mean", "sum")
 
 
@@ -111,6 +113,13 @@ def kl_rows(logP, target, valid, eps):
     return L
 
 
+def ce_rows(logP, labels, valid):
+    """Per-row cross-entropy -log p(y_r): the KL head with a one-hot target
+    (q log q vanishes), the fused linear cross-entropy head the
+    FusedLinearKLDivLoss page (Summary) takes its chunk geometry from."""
+    return -selective_rows(logP, labels, valid)
+
+
 def selective_rows(logP, labels, valid):
     """Per-row selective log-prob log p(y_r) of the label.
 
@@ -134,8 +143,10 @@ def reduction_scale(head, reduction, n_valid, V):
     the semantics of ``torch.nn.KLDivLoss`` (batchmean divides by the batch,
     mean by the element count, sum by 1); ``"none"`` is refused because
     gradient-in-forward needs a scalar loss. With ignored rows the batch is the
-    valid rows. For the selective head the tokens are the batch, so mean and
-    batchmean both divide by the valid-token count. No valid row gives g = 0.
+    valid rows. For the selective and cross-entropy heads the tokens are the
+    batch, so mean and batchmean both divide by the valid-token count (the
+    ``torch.nn.functional.cross_entropy`` mean with ``ignore_index``). No valid
+    row gives g = 0.
     """
     if reduction not in REDUCTIONS:
         raise ValueError(f"unsupported reduction {reduction!r}")
@@ -149,8 +160,9 @@ def reduction_scale(head, reduction, n_valid, V):
 
 
 def row_weights(head, weights, BT):
-    """Per-row loss weights: the advantages of the selective head, else 1."""
-    if head == HEAD_SELECTIVE and weights is not None:
+    """Per-row loss weights: the advantages of the selective head (optional
+    per-token weights of the cross-entropy head), else 1."""
+    if head in (HEAD_SELECTIVE, HEAD_CE) and weights is not None:
         return _f64(weights)
     return np.ones(BT)
 
@@ -161,6 +173,7 @@ def dlogits(head, logP, target, labels, w, valid, g, temperature):
     With P = exp(logP) and S = Z / tau:
       KL:        dS_r = g * (Q_r * P_r - q_r),   Q_r = sum_v q_rv
       SELECTIVE: dS_r = g * w_r * (onehot(y_r) - P_r)
+      CE:        dS_r = g * w_r * (P_r - onehot(y_r))
     and dZ = dS / tau. Ignored rows are 0. This is the log-softmax backward
     the FusedLinearKLDivLoss page (Details) computes in place on the saved
     log-probs; Q_r keeps it exact even when a target row does not sum to 1.
@@ -178,7 +191,8 @@ def dlogits(head, logP, target, labels, w, valid, g, temperature):
             y = np.asarray(labels)[r]
             onehot = np.zeros_like(P)
             onehot[np.arange(r.size), y] = 1.0
-            dS[r] = g * w[r][:, None] * (onehot - P)
+            sign = -1.0 if head == HEAD_CE else 1.0
+            dS[r] = sign * g * w[r][:, None] * (onehot - P)
     return dS / float(temperature)
 
 
@@ -194,10 +208,10 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
     autograd asks for; LoRA normalization page, Key Changes: COMPUTE_DW and
     COMPUTE_DB prune weight and bias gradients independently).
 
-    Returns a dict with loss (float), per_row [BT] (KL_r or log p(y_r); 0 on
-    ignored rows), dX [BT, H], dW [V, H] or None, db [V] or None, n_valid, g.
+    Returns a dict with loss (float), per_row [BT] (KL_r, log p(y_r) or
+    -log p(y_r); 0 on ignored rows), dX [BT, H], dW [V, H] or None, db [V] or None, n_valid, g.
     """
-    if head not in (HEAD_KL, HEAD_SELECTIVE):
+    if head not in (HEAD_KL, HEAD_SELECTIVE, HEAD_CE):
         raise ValueError(f"unknown head {head!r}")
     if not (temperature > 0 and np.isfinite(temperature)):
         raise ValueError("temperature must be positive and finite")
@@ -219,8 +233,8 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
         L = kl_rows(logP, target, valid, eps)
     else:
         if labels is None:
-            raise ValueError("the selective head needs labels")
-        L = selective_rows(logP, labels, valid)
+            raise ValueError("the selective and cross-entropy heads need labels")
+        L = (ce_rows if head == HEAD_CE else selective_rows)(logP, labels, valid)
     loss = g * float((w * L).sum())
 
     dZ = dlogits(head, logP, target, labels, w, valid, g, temperature)
@@ -258,6 +272,8 @@ def sampled_rows(X_rows, W, b=None, *, head, n_valid, labels_rows=None,
     logP, _ = log_softmax(S)
     if head == HEAD_KL:
         L = kl_rows(logP, target_rows, valid, eps)
+    elif head == HEAD_CE:
+        L = ce_rows(logP, labels_rows, valid)
     else:
         L = selective_rows(logP, labels_rows, valid)
     dZ = dlogits(head, logP, target_rows, labels_rows, w, valid, g, temperature)

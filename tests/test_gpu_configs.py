@@ -39,14 +39,20 @@ def test_cfg2_full():
     H.compare_full(out, ref, case)
 
 
-@pytest.mark.parametrize("cfg", [3, 4, 5])
+# The fused linear cross-entropy head at the llama-3 head shape of the
+# V=128256 GRPO workload, with a trainable head (beyond the five workloads).
+CE_FULL = workloads.CONFIGS[3].replace(name="ce-bf16-trainable-B8T1024-V128256", head="ce",
+                                       compute_dW=True, ignore_frac=0.05, seed=6)
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5, "ce"])
 def test_full_config_sampled(cfg):
-    case = workloads.CONFIGS[cfg]
+    case = CE_FULL if cfg == "ce" else workloads.CONFIGS[cfg]
     print(f"[cfg{cfg}] {case}", flush=True)
     inp = H.make(case)
     out = H.run_gpu(inp, case)
     labels = inp["labels"]
-    rows = workloads.row_sample(case.BT, 24, seed=100 + cfg, labels=labels)
+    rows = workloads.row_sample(case.BT, 24, seed=100 + case.seed, labels=labels)
     n_valid = case.BT if labels is None else int((labels != case.ignore_index).sum())
     ref = fll_oracle.sampled_rows(
         H.to_np(inp["X"][rows]), H.to_np(inp["W"]), H.to_np(inp["b"]), head=case.head,

@@ -37,6 +37,12 @@ SMALL = {
         BT=130, H=72, V=333, dtype="fp32", head="selective", has_bias=True,
         compute_dW=True, compute_db=True, reduction="batchmean", x_std=1.0, w_std=0.1,
         seed=15),
+    "ce-bf16-ragged-trainable-bias": workloads.small_case(
+        BT=300, H=264, V=1000, dtype="bf16", head="ce", has_bias=True, compute_dW=True,
+        compute_db=True, reduction="mean", ignore_frac=0.1, w_std=0.05, seed=17),
+    "ce-fp32-sum-tau": workloads.small_case(
+        BT=90, H=48, V=301, dtype="fp32", head="ce", compute_dW=True, reduction="sum",
+        temperature=0.5, x_std=1.0, w_std=0.1, seed=18),
     "kl-fp32-sum-ignored": workloads.small_case(
         BT=100, H=40, V=515, dtype="fp32", head="kl", reduction="sum", ignore_frac=0.2,
         compute_dW=True, x_std=1.0, w_std=0.1, temperature=0.75, seed=16),
@@ -205,3 +211,12 @@ def test_temperature_power_of_two_identity():
     assert torch.equal(a["loss"], b["loss"])
     torch.testing.assert_close(a["dX"].float(), b["dX"].float(), rtol=0, atol=0)
     torch.testing.assert_close(a["dW"], b["dW"] / 2, rtol=0, atol=0)
+
+
+def test_ce_per_token_weights():
+    case = workloads.small_case(BT=200, H=64, V=513, dtype="fp32", head="ce",
+                                compute_dW=True, reduction="mean", x_std=1.0,
+                                w_std=0.1, seed=25)
+    inp = H.make(case)
+    inp["weights"] = torch.rand(case.BT, generator=torch.Generator().manual_seed(7))
+    H.compare_full(H.run_gpu(inp, case), H.run_oracle(inp, case), case)

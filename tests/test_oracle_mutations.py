@@ -54,6 +54,11 @@ def _dlogits_q_normalised(head, logP, target, labels, w, valid, g, temperature):
     return dS / temperature
 
 
+def _dlogits_ce_sign_of_selective(head, logP, target, labels, w, valid, g, temperature):
+    h = "selective" if head == "ce" else head
+    return _orig["dlogits"](h, logP, target, labels, w, valid, g, temperature)
+
+
 def _dlogits_wrong_sign(head, logP, target, labels, w, valid, g, temperature):
     return -_orig["dlogits"](head, logP, target, labels, w, valid, g, temperature)
 
@@ -91,6 +96,7 @@ MUTATIONS = {
     "dZ misses 1/tau": ("dlogits", _dlogits_no_tau),
     "KL grad assumes sum q = 1": ("dlogits", _dlogits_q_normalised),
     "gradient sign flipped": ("dlogits", _dlogits_wrong_sign),
+    "CE gradient takes the selective sign": ("dlogits", _dlogits_ce_sign_of_selective),
     "KL mean ignores V": ("reduction_scale", _scale_mean_ignores_V),
     "ignored rows counted": ("reduction_scale", _scale_counts_ignored),
     "bias dropped": ("logits", _logits_drop_bias),

@@ -101,8 +101,10 @@ def test_kl_zero_when_target_is_model_softmax():
         q = _softmax(S)
         out = O.fwd_bwd(X, W, b, head="kl", target=q, temperature=tau,
                         reduction="sum")
-        # logits reach |S| ~ 20 here, so fp64 rounding leaves ~1e-12
-        assert abs(out["loss"]) < 1e-11
+        # KL = sum q log q - sum q log p cancels two sums of size ~|S|; fp64
+        # rounding leaves a few ulps of their magnitude
+        scale = float(np.abs(q * np.log(q)).sum() + np.abs(q * S).sum())
+        assert abs(out["loss"]) < 1e-14 * max(scale, 1.0) * 100
         assert np.abs(out["dX"]).max() < 1e-13
         assert np.abs(out["dW"]).max() < 1e-13
         assert np.abs(out["db"]).max() < 1e-13
@@ -256,7 +258,7 @@ def _central_fd(f, args, i, h=1e-6):
 
 
 FD_CASES = []
-for head in ("kl", "selective"):
+for head in ("kl", "selective", "ce"):
     for reduction in ("batchmean", "mean", "sum"):
         for tau in (0.5, 1.0, 2.0):
             FD_CASES.append((head, reduction, tau))
@@ -282,7 +284,7 @@ def test_gradients_central_differences(head, reduction, tau):
                                    err_msg=name)
 
 
-@pytest.mark.parametrize("head", ["kl", "selective"])
+@pytest.mark.parametrize("head", ["kl", "selective", "ce"])
 def test_gradients_match_torch_autograd(head):
     BT, H, V, tau = 33, 24, 57, 2.0
     X, W, b = _rand(BT, H), _rand(V, H, std=0.3), _rand(V)
@@ -296,12 +298,16 @@ def test_gradients_match_torch_autograd(head):
         loss_t = F.kl_div(logP[torch.tensor(keep)], torch.tensor(q[keep]),
                           reduction="batchmean")
         kw = dict(target=q, reduction="batchmean")
-    else:
+    elif head == "selective":
         w = _rand(BT)
         ce = F.cross_entropy(F.linear(Xt, Wt, bt) / tau, torch.tensor(labels),
                              ignore_index=-100, reduction="none")
         loss_t = -(torch.tensor(w) * ce).sum() / keep.sum()
         kw = dict(weights=w, reduction="mean")
+    else:
+        loss_t = F.cross_entropy(F.linear(Xt, Wt, bt) / tau, torch.tensor(labels),
+                                 ignore_index=-100, reduction="mean")
+        kw = dict(reduction="mean")
     loss_t.backward()
     out = O.fwd_bwd(X, W, b, head=head, labels=labels, temperature=tau, **kw)
     assert out["loss"] == pytest.approx(float(loss_t), rel=1e-12)
@@ -371,3 +377,44 @@ def test_sampled_rows_agree_with_full(head):
                          weights_rows=None if w is None else w[rows], **kw)
     np.testing.assert_array_equal(sub["per_row"], full["per_row"][rows])
     np.testing.assert_allclose(sub["dX"], full["dX"][rows], rtol=1e-14, atol=1e-17)
+
+
+# --------------------------------------------------------------------------
+# cross-entropy head
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_ce_matches_torch_cross_entropy(reduction):
+    X, W, b = _rand(12, 6), _rand(19, 6), _rand(19)
+    y = rng.integers(0, 19, size=12)
+    y[[2, 7]] = -100
+    for tau in (0.5, 1.0):
+        out = O.fwd_bwd(X, W, b, head="ce", labels=y, temperature=tau, reduction=reduction)
+        ref = F.cross_entropy(torch.tensor(O.logits(X, W, b, tau)), torch.tensor(y),
+                              ignore_index=-100, reduction=reduction)
+        assert out["loss"] == pytest.approx(float(ref), rel=1e-13)
+        assert (out["per_row"] >= 0).all()
+
+
+def test_ce_weighted_matches_torch():
+    X, W = _rand(10, 5), _rand(13, 5)
+    y = rng.integers(0, 13, size=10)
+    w = np.abs(_rand(10))
+    out = O.fwd_bwd(X, W, head="ce", labels=y, weights=w, reduction="sum")
+    ce = F.cross_entropy(torch.tensor(O.logits(X, W, None, 1.0)), torch.tensor(y),
+                         reduction="none")
+    assert out["loss"] == pytest.approx(float((torch.tensor(w) * ce).sum()), rel=1e-13)
+
+
+def test_ce_equals_kl_with_one_hot_target():
+    # cross-entropy is the KL head against a one-hot target (q log q = 0)
+    X, W, b = _rand(9, 7), _rand(15, 7), _rand(15)
+    y = rng.integers(0, 15, size=9)
+    q = np.zeros((9, 15))
+    q[np.arange(9), y] = 1.0
+    for tau in (0.5, 2.0):
+        a = O.fwd_bwd(X, W, b, head="ce", labels=y, temperature=tau, reduction="sum")
+        c = O.fwd_bwd(X, W, b, head="kl", target=q, temperature=tau, reduction="sum")
+        assert a["loss"] == pytest.approx(c["loss"], rel=1e-13)
+        for k in ("dX", "dW", "db"):
+            np.testing.assert_allclose(a[k], c[k], rtol=1e-12, atol=1e-15, err_msg=k)

@@ -28,6 +28,7 @@ import torch
 
 HEAD_KL = "kl"
 HEAD_SELECTIVE = "selective"
+HEAD_CE = "ce"
 
 IGNORE_INDEX = -100
 
@@ -41,7 +42,7 @@ class Case:
     H: int
     V: int
     dtype: str  # "bf16" or "fp32"
-    head: str  # HEAD_KL or HEAD_SELECTIVE
+    head: str  # HEAD_KL, HEAD_SELECTIVE or HEAD_CE
     has_bias: bool = False
     compute_dW: bool = False
     compute_db: bool = False
@@ -49,7 +50,7 @@ class Case:
     temperature: float = 1.0
     ignore_frac: float = 0.0
     with_labels: bool = True  # KL: labels act only as an ignore mask
-    with_weights: bool = True  # selective head: per-token advantages
+    with_weights: bool = True  # selective head: per-token advantages (never for CE)
     x_std: float = 1.0
     w_std: float = 0.02
     b_std: float = 0.01
@@ -116,7 +117,8 @@ def make_inputs(case: Case) -> dict:
         del tl
 
     labels = None
-    need_labels = case.head == HEAD_SELECTIVE or case.with_labels or case.ignore_frac > 0
+    need_labels = (case.head in (HEAD_SELECTIVE, HEAD_CE) or case.with_labels
+                   or case.ignore_frac > 0)
     if need_labels:
         labels = torch.randint(0, V, (BT,), generator=gen, dtype=torch.int64)
 
