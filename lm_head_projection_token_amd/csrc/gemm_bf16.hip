@@ -56,6 +56,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -71,6 +72,10 @@ constexpr int kLoadsPerStage = 8;               // per thread: 4 for A, 4 for B
 // the A half of the newest one (prologue: the later full stages only).
 constexpr int kVmcntLoop = kLoadsPerStage * (NSTAGE - 3) + kLoadsPerStage / 2;
 constexpr int kVmcntPrologue = kLoadsPerStage * (NSTAGE - 2);
+// Epilogue slab: 32 rows of the wave's 128 fp32 columns, rows 528 bytes apart.
+constexpr int kSlabPitch = 132;                     // floats
+constexpr int kSlabBytes = 32 * kSlabPitch * 4;     // 16896 per wave
+static_assert(4 * kSlabBytes <= NSTAGE * kStageBytes, "epilogue slabs reuse the stages");
 constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
 constexpr unsigned kMaxRecords = 0x7fffffffu;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
@@ -101,10 +106,12 @@ struct OpK {
   int64_t ld, row0, nrows;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
   int kc[4];         // their K offsets within the slice
-  unsigned fa[2];    // fragment read byte offsets (half-step 0 and 1)
+  unsigned fa[2];    // LDS addresses of the fragment reads (half-step 0 and 1)
+  unsigned fa_hi[2]; // the same + 64 KB (stages past the 16-bit read offset)
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
-                                       int64_t nrows_, int wave, int lane, int wr) {
+                                       int64_t nrows_, int wave, int lane, int wr,
+                                       unsigned lds_base) {
     p = p_;
     ld = ld_;
     row0 = row0_;
@@ -120,26 +127,29 @@ struct OpK {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = 2 * h + (lane >> 5);
-      fa[h] = unsigned(r * 64 + 16 * (c ^ swz_k(r)));
+      fa[h] = lds_base + unsigned(r * 64 + 16 * (c ^ swz_k(r)));
+      fa_hi[h] = fa[h] + 65536u;
     }
   }
+  // Load chunk i of this thread's share of the slice starting at K = k0 into
+  // the stage at LDS byte offset `stage`. CHECK: the slice may end before
+  // k0 + BK, so chunks past kend are pointed outside the descriptor.
+  template <bool CHECK>
   __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
                                             int64_t kend) const {
     const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
-    const unsigned v = (k0 + kc[i] < kend) ? voff[i] : kOOB;
+    const unsigned v = (!CHECK || k0 + kc[i] < kend) ? voff[i] : kOOB;
     load_lds16(r, stage + (wave * 4 + i) * 1024, v);
   }
-  __device__ __forceinline__ void issue(LDS_AS char *stage, int wave, int64_t k0,
-                                        int64_t kend) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_one(stage, wave, i, k0, kend);
-  }
   static constexpr int kReads = 4;  // LDS reads per half-step
-  // Read number x (0..3) of a half-step: block x (rows wr + 32 x ...).
-  __device__ __forceinline__ void read(bf16x8 (&f)[4], const LDS_AS char *stage, int x,
-                                       int h) const {
-    const LDS_AS char *b = stage + fa[h] + x * 2048;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(f[x]) : "v"(b));
+  // Read number X (0..3) of half-step H from the stage at LDS byte offset OFF:
+  // block X (rows wr + 32 X ...). The stage and block offsets are immediates.
+  template <int OFF, int X, int H>
+  __device__ __forceinline__ void read(bf16x8 (&f)[4]) const {
+    const unsigned base = OFF >= 65536 ? fa_hi[H] : fa[H];
+    asm volatile("ds_read_b128 %0, %1 offset:%2"
+                 : "=v"(f[X])
+                 : "v"(base), "i"(OFF % 65536 + X * 2048));
   }
 };
 
@@ -148,10 +158,11 @@ struct OpMN {
   const unsigned short *p;
   int64_t ld, col0;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (k0, col0)
-  unsigned fb[4];    // transpose-read byte offsets, block i (half-step 0, h 0)
+  unsigned fb[4];    // LDS addresses of the transpose reads, block i (half-step 0)
+  unsigned fb_hi[4]; // the same + 64 KB
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t col0_,
-                                       int wave, int lane, int wr) {
+                                       int wave, int lane, int wr, unsigned lds_base) {
     p = p_;
     ld = ld_;
     col0 = col0_;
@@ -169,30 +180,32 @@ struct OpMN {
     for (int i = 0; i < 4; ++i) {
       const int col = wr + 32 * i + 16 * (G & 1) + 4 * (q & 3);
       const int c = col >> 3, half = (col >> 2) & 1;
-      fb[i] = unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
+      fb[i] = lds_base + unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
+      fb_hi[i] = fb[i] + 65536u;
     }
   }
+  // K-rows past kend lie outside the descriptor and read as zero, so no
+  // per-lane check is needed.
+  template <bool CHECK>
   __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
                                             int64_t kend) const {
     const __amdgpu_buffer_rsrc_t r = rsrc(p + k0 * ld + col0, ((kend - k0) * ld - col0) * 2);
     load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
   }
-  __device__ __forceinline__ void issue(LDS_AS char *stage, int wave, int64_t k0,
-                                        int64_t kend) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_one(stage, wave, i, k0, kend);
-  }
   static constexpr int kReads = 8;  // LDS reads per half-step
-  // Read number x (0..7) of a half-step: block x / 2, K-values 4 (x % 2) .. + 3
-  // of each lane's eight (the two halves of the MFMA operand).
-  __device__ __forceinline__ void read(bf16x8 (&f)[4], const LDS_AS char *stage, int x,
-                                       int h) const {
-    const int i = x >> 1;
-    const LDS_AS char *b = stage + fb[i] + h * 16 * 512 + (x & 1) * 4 * 512;
+  // Read number X (0..7) of half-step H from the stage at LDS byte offset
+  // OFF: block X / 2, K-values 4 (X % 2) .. + 3 of each lane's eight (the two
+  // halves of the MFMA operand).
+  template <int OFF, int X, int H>
+  __device__ __forceinline__ void read(bf16x8 (&f)[4]) const {
+    constexpr int i = X >> 1;
+    const unsigned base = OFF >= 65536 ? fb_hi[i] : fb[i];
     i16x4 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(b));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(v)
+                 : "v"(base), "i"(OFF % 65536 + H * 16 * 512 + (X & 1) * 4 * 512));
     auto w = __builtin_bit_cast(i16x8, f[i]);
-    if (x & 1) {
+    if constexpr (X & 1) {
       w = __builtin_shufflevector(w, __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1),
                                   0, 1, 2, 3, 8, 9, 10, 11);
     } else {
@@ -202,6 +215,15 @@ struct OpMN {
     f[i] = __builtin_bit_cast(bf16x8, w);
   }
 };
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
 
 struct GemmDesc {
   const unsigned short *A;
@@ -231,6 +253,22 @@ struct EpiLogits {
   __device__ __forceinline__ float col_bias(int64_t n) const {
     return bias ? __uint_as_float(unsigned(bias[n]) << 16) : 0.0f;
   }
+  // store4_in: the four columns are inside the matrix
+  __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int) const {
+    *reinterpret_cast<f32x4 *>(S + m * lds + n) = v;
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,
+                                         int) const {
+    float *p = S + m * lds + n;
+    if (n + 4 <= nmax) {
+      *reinterpret_cast<float4 *>(p) = v;
+    } else {
+      const float ve[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < nmax) p[e] = ve[e];
+    }
+  }
 };
 
 __device__ __forceinline__ unsigned short f2bf(float f) {
@@ -249,6 +287,16 @@ struct EpiDx {
   int64_t ldo;
   float *partial;
   int64_t M, N;
+  __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int split) const {
+    if (partial) {
+      *reinterpret_cast<f32x4 *>(partial + (int64_t(split) * M + m) * N + n) = v;
+    } else {
+      uint2 pk;
+      pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
+      pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+      *reinterpret_cast<uint2 *>(out + m * ldo + n) = pk;
+    }
+  }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,
                                          int split) const {
     const float ve[4] = {v.x, v.y, v.z, v.w};
@@ -257,6 +305,7 @@ struct EpiDx {
       if (n + 4 <= nmax) {
         *reinterpret_cast<float4 *>(p) = v;
       } else {
+#pragma unroll
         for (int e = 0; e < 4; ++e)
           if (n + e < nmax) p[e] = ve[e];
       }
@@ -268,6 +317,7 @@ struct EpiDx {
         pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
         *reinterpret_cast<uint2 *>(p) = pk;
       } else {
+#pragma unroll
         for (int e = 0; e < 4; ++e)
           if (n + e < nmax) p[e] = f2bf(ve[e]);
       }
@@ -283,6 +333,13 @@ struct EpiDw {
   float *dW;
   int64_t ld;
   int accumulate;
+  __device__ __forceinline__ f32x4 load4_in(int64_t m, int64_t n) const {
+    if (!accumulate) return f32x4{0.f, 0.f, 0.f, 0.f};
+    return *reinterpret_cast<const f32x4 *>(dW + m * ld + n);
+  }
+  __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int) const {
+    *reinterpret_cast<f32x4 *>(dW + m * ld + n) = v;
+  }
   __device__ __forceinline__ float4 load4(int64_t m, int64_t n, int64_t nmax) const {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!accumulate) return v;
@@ -300,6 +357,7 @@ struct EpiDw {
       *reinterpret_cast<float4 *>(p) = v;
     } else {
       const float ve[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
       for (int e = 0; e < 4; ++e)
         if (n + e < nmax) p[e] = ve[e];
     }
@@ -315,11 +373,20 @@ struct EpiDw {
 __device__ __forceinline__ void mfma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// max of three floats (v_max3_f32). fmaxf on values read from accumulator
+// registers would first quiet each input with an extra v_max_f32 copy.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
+  __shared__ __attribute__((aligned(16))) float btab_[Epi::kRowStats ? BN : 1];
+  LDS_AS float *btab = (LDS_AS float *)btab_;
   LDS_AS char *lds = (LDS_AS char *)smem;
 
   // ---- tile: optional XCD remap, then grouped order ----
@@ -357,17 +424,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int64_t kend = min(d.K, kbeg + d.split_len);
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  // The wavefront index is uniform: in a scalar register, every LDS
+  // destination of the staging loads is scalar arithmetic.
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const unsigned lds_base = unsigned(reinterpret_cast<uintptr_t>(lds));
 
   using OA = typename std::conditional<A_K, OpK, OpMN>::type;
   using OB = typename std::conditional<B_K, OpK, OpMN>::type;
   OA opa;
   OB opb;
-  if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, wave, lane, wm * 128);
-  else opa.init(d.A, d.lda, m0, wave, lane, wm * 128);
-  if constexpr (B_K) opb.init(d.B, d.ldb, n0, d.N, wave, lane, wn * 128);
-  else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128);
+  if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, wave, lane, wm * 128, lds_base);
+  else opa.init(d.A, d.lda, m0, wave, lane, wm * 128, lds_base);
+  if constexpr (B_K) opb.init(d.B, d.ldb, n0, d.N, wave, lane, wn * 128, lds_base + kOperandBytes);
+  else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128, lds_base + kOperandBytes);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -377,19 +448,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][k][e] = 0.0f;
 
+  // K-step kt (the last one may be partial) computes from stage kt % NSTAGE
+  // and loads the slice of K-step kt + NSTAGE - 1. The loop is unrolled by
+  // NSTAGE, so every stage offset below is a compile-time constant.
   const int nkt = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
-  auto stageA = [&](int s) { return lds + (s % NSTAGE) * kStageBytes; };
-  auto stageB = [&](int s) { return lds + (s % NSTAGE) * kStageBytes + kOperandBytes; };
-  auto issue = [&](int s) {
-    const int64_t k0 = kbeg + int64_t(s) * BK;
-    opa.issue(stageA(s), wave, k0, kend);
-    opb.issue(stageB(s), wave, k0, kend);
-  };
+  const int nkt_full = kend > kbeg ? int((kend - kbeg) / BK) : 0;
 
   if (nkt > 0) {
-    // prologue: three stages in flight, wait for the first
+    // prologue: NSTAGE - 1 stages in flight, wait for the first
+    static_for<NSTAGE - 1>([&](auto S) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value;
+      const int64_t k0 = kbeg + int64_t(s) * BK;
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s) issue(s);
+      for (int q = 0; q < 4; ++q) {
+        opa.template issue_one<true>(lds + s * kStageBytes, wave, q, k0, kend);
+        opb.template issue_one<true>(lds + s * kStageBytes + kOperandBytes, wave, q, k0, kend);
+      }
+    });
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntPrologue) : "memory");
     __builtin_amdgcn_s_barrier();
   }
@@ -401,152 +476,234 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     fb[0][i] = fb[1][i] = bf16x8{};
   }
   if (nkt > 0) {
-#pragma unroll
-    for (int x = 0; x < OA::kReads; ++x) opa.read(fa[0], stageA(0), x, 0);
-#pragma unroll
-    for (int x = 0; x < OB::kReads; ++x) opb.read(fb[0], stageB(0), x, 0);
+    static_for<OA::kReads>([&](auto X) __attribute__((always_inline)) {
+      opa.template read<0, decltype(X)::value, 0>(fa[0]);
+    });
+    static_for<OB::kReads>([&](auto X) __attribute__((always_inline)) {
+      opb.template read<0, decltype(X)::value, 0>(fb[0]);
+    });
   }
 
   // One half-step: 16 MFMAs on (ca, cb); between them the reads of (na, nb)
-  // from the given stages and, after MFMAs 0, 4, 8, 12, one stage load each.
-  auto half = [&](bf16x8 (&ca)[4], bf16x8 (&cb)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
-                  const LDS_AS char *sa, const LDS_AS char *sb, int h, auto &&load) {
+  // (half-step H of the stage at offset OFF) and, after MFMAs 0, 4, 8, 12,
+  // one staging load each.
+  auto half = [&](auto OFF_, auto H_, bf16x8(&ca)[4], bf16x8(&cb)[4], bf16x8(&na)[4],
+                  bf16x8(&nb)[4], auto &&load) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(OFF_)::value, H = decltype(H_)::value;
     constexpr int ea = 16 / OA::kReads, eb = 16 / OB::kReads;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
+    static_for<16>([&](auto X_) __attribute__((always_inline)) {
+      constexpr int x = decltype(X_)::value;
       mfma(acc[x >> 2][x & 3], cb[x & 3], ca[x >> 2]);
-      if (x % ea == 0) opa.read(na, sa, x / ea, h);
-      if (x % eb == eb / 2) opb.read(nb, sb, x / eb, h);
-      if ((x & 3) == 0) load(x >> 2);
-    }
+      if constexpr (x % ea == 0) opa.template read<OFF, x / ea, H>(na);
+      if constexpr (x % eb == eb / 2) opb.template read<OFF, x / eb, H>(nb);
+      if constexpr ((x & 3) == 0) load(x >> 2);
+    });
   };
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  auto kstep = [&](auto U_, auto CHECK_, int kt) __attribute__((always_inline)) {
+    constexpr int u = decltype(U_)::value;
+    constexpr bool CHECK = decltype(CHECK_)::value;
+    constexpr int s_cur = u * kStageBytes;
+    constexpr int s_nxt = ((u + 1) % NSTAGE) * kStageBytes;
+    constexpr int s_pre = ((u + NSTAGE - 1) % NSTAGE) * kStageBytes;
     const int64_t k_next = kbeg + int64_t(kt + NSTAGE - 1) * BK;
     // [B] half-step 0 of stage kt; read half-step 1 of stage kt; request the
-    // A slice of stage kt + NSTAGE - 1 (past the end: zero-filled, unread).
+    // A slice of K-step kt + NSTAGE - 1 (past the end: zero-filled, unread).
     wait_lds();
-    half(fa[0], fb[0], fa[1], fb[1], stageA(kt), stageB(kt), 1,
-         [&](int q) { opa.issue_one(stageA(kt + NSTAGE - 1), wave, q, k_next, kend); });
+    half(std::integral_constant<int, s_cur>{}, std::integral_constant<int, 1>{}, fa[0], fb[0],
+         fa[1], fb[1], [&](int q) __attribute__((always_inline)) {
+           opa.template issue_one<CHECK>(lds + s_pre, wave, q, k_next, kend);
+         });
     // [C] stage kt + 1 complete in LDS for every wave: of the loads issued so
-    // far only the later stages (8 per thread each) and the A half of stage
+    // far only the later stages (8 per thread each) and the A half of K-step
     // kt + NSTAGE - 1 (4) may still be in flight.
     wait_lds();
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntLoop) : "memory");
     __builtin_amdgcn_s_barrier();
     // [D] half-step 1 of stage kt; read half-step 0 of stage kt + 1; request
-    // the B slice of stage kt + NSTAGE - 1.
-    half(fa[1], fb[1], fa[0], fb[0], stageA(kt + 1), stageB(kt + 1), 0,
-         [&](int q) { opb.issue_one(stageB(kt + NSTAGE - 1), wave, q, k_next, kend); });
-  }
+    // the B slice of K-step kt + NSTAGE - 1.
+    half(std::integral_constant<int, s_nxt>{}, std::integral_constant<int, 0>{}, fa[1], fb[1],
+         fa[0], fb[0], [&](int q) __attribute__((always_inline)) {
+           opb.template issue_one<CHECK>(lds + s_pre + kOperandBytes, wave, q, k_next, kend);
+         });
+  };
+
+  // Full-speed steps: the slice each one requests lies wholly before kend.
+  const int fast_end = nkt_full - (NSTAGE - 1);
+  int kt = 0;
+  for (; kt + NSTAGE <= fast_end; kt += NSTAGE)
+    static_for<NSTAGE>([&](auto U) __attribute__((always_inline)) {
+      kstep(U, std::false_type{}, kt + decltype(U)::value);
+    });
+  // The last steps request partial or empty slices.
+  for (; kt < nkt; kt += NSTAGE)
+    static_for<NSTAGE>([&](auto U) __attribute__((always_inline)) {
+      if (kt + decltype(U)::value < nkt) kstep(U, std::true_type{}, kt + decltype(U)::value);
+    });
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // The MFMAs take the B fragment as their first operand, so each 32 x 32
   // accumulator block holds the transposed product: lane l owns output row
   // m = l % 32 of the block, and register r holds column
   // 8 (r / 4) + 4 (l / 32) + r % 4. A lane therefore owns, for each of its
-  // four rows, 64 of the wave's 128 columns in runs of four (16-byte
-  // stores), and lane l ^ 32 owns the other 64.
+  // four rows, 64 of the wave's 128 columns in runs of four, and lane l ^ 32
+  // owns the other 64.
+  //
+  // Stored as they lie, a 64-lane store would write 32 rows x 32 bytes, a
+  // quarter of a cache line per row; the write path then runs far below its
+  // rate. So each 32-row slab of the wave's tile passes through LDS (the
+  // staging buffers are idle now): written in the accumulator layout, read
+  // back so that one instruction covers two rows x 128 columns, i.e. 512
+  // contiguous bytes per row. Rows of the slab sit 528 bytes apart in LDS,
+  // which spreads both the writes and the reads over all banks.
+  // The bias of the tile's 256 columns (0 past N) goes to LDS: read per slab,
+  // it is not held in registers across the epilogue.
+  if constexpr (Epi::kRowStats) {
+    if (epi.bias) btab[t] = n0 + t < d.N ? epi.col_bias(n0 + t) : 0.0f;
+  }
+  __syncthreads();  // every wave is done reading the staging buffers
+  LDS_AS float *slab = (LDS_AS float *)(lds + wave * kSlabBytes);
   const int lrow = lane & 31;
   const int lcol = 4 * (lane >> 5);
-  if constexpr (Epi::kRowStats) {
-    const int64_t nh = n0 + wn * 128;  // first column of this 128-column half-tile
-    float bias[4][4][4];
+  const int crow = lane >> 5;        // coalesced layout: row 2 j + crow of the slab,
+  const int ccol = 4 * (lane & 31);  // columns ccol .. ccol + 3 of the wave's 128
+  const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
+
+  // every column of this wave is below N / every row and column is inside
+  const bool full = nw + 128 <= d.N;
+  const bool interior = full && mw + 128 <= d.M;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // dW: the old values of slabs i and i + 1 are in flight while slab i is
+  // transposed and stored.
+  f32x4 old[2][16];
+  auto load_old = [&](int i, f32x4(&o)[16]) __attribute__((always_inline)) {
+    if constexpr (Epi::kReadModifyWrite) {
+      int64_t mrow = mw + i * 32 + crow;
+      asm volatile("" : "+v"(mrow));
+      if (interior) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[j] = epi.load4_in(mrow + 2 * j, nw + ccol);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float4 t = mrow + 2 * j < d.M ? epi.load4(mrow + 2 * j, nw + ccol, d.N)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+          o[j] = f32x4{t.x, t.y, t.z, t.w};
+        }
+      }
+    }
+  };
+  if constexpr (Epi::kReadModifyWrite) {
+    load_old(0, old[0]);
+    load_old(1, old[1]);
+  }
+
+  // One 32-row slab; I is a compile-time constant so that acc[I] stays in
+  // registers (a runtime index would move the accumulators to scratch).
+  auto do_slab = [&](auto I_) __attribute__((always_inline)) {
+    constexpr int i = decltype(I_)::value;
+    // keep each slab's register working set to itself
+    __builtin_amdgcn_sched_barrier(0);
+    // this lane's 64 values of the slab: v[4 k + q] = columns k * 32 + 8 q + lcol + 0..3
+    f32x4 v[16];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
+        v[4 * k + q] = f32x4{acc[i][k][4 * q + 0], acc[i][k][4 * q + 1], acc[i][k][4 * q + 2],
+                             acc[i][k][4 * q + 3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t n = nh + k * 32 + 8 * q + lcol + e;
-          bias[k][q][e] = n < d.N ? epi.col_bias(n) : 0.0f;
+    for (int c = 0; c < 16; ++c) asm volatile("" : "+v"(v[c]));  // copied here, not earlier
+    if constexpr (Epi::kRowStats) {
+      // S = (acc + b) / tau, then this row's max and sum of exp over the
+      // wave's 128 columns below N, merged with lane l ^ 32.
+      const int64_t m = mw + i * 32 + lrow;
+      if (epi.bias) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const f32x4 b =
+              *(const LDS_AS f32x4 *)(btab + wn * 128 + (c >> 2) * 32 + 8 * (c & 3) + lcol);
+          v[c] = (v[c] + b) * epi.inv_tau;
         }
+      } else if (epi.inv_tau != 1.0f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 128 + i * 32 + lrow;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = nh + k * 32 + 8 * q + lcol;
-          float4 v;
-          v.x = (acc[i][k][4 * q + 0] + bias[k][q][0]) * epi.inv_tau;
-          v.y = (acc[i][k][4 * q + 1] + bias[k][q][1]) * epi.inv_tau;
-          v.z = (acc[i][k][4 * q + 2] + bias[k][q][2]) * epi.inv_tau;
-          v.w = (acc[i][k][4 * q + 3] + bias[k][q][3]) * epi.inv_tau;
-          acc[i][k][4 * q + 0] = v.x;
-          acc[i][k][4 * q + 1] = v.y;
-          acc[i][k][4 * q + 2] = v.z;
-          acc[i][k][4 * q + 3] = v.w;
-          float *dst = epi.S + m * epi.lds + n;
-          if (n + 4 <= d.N) {
-            if (m < d.M) *reinterpret_cast<float4 *>(dst) = v;
-            mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-          } else {
-            const float ve[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < d.N) {
-                if (m < d.M) dst[e] = ve[e];
-                mx = fmaxf(mx, ve[e]);
-              }
-          }
-        }
+        for (int c = 0; c < 16; ++c) v[c] *= epi.inv_tau;
       }
       if (epi.stats) {
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        float se = 0.0f;
-        if (mx != -INFINITY) {
+        // column of element e of v[c]: nw + (c >> 2) * 32 + 8 (c & 3) + lcol + e
+        float mx = -INFINITY;
+        if (full) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (nh + k * 32 + 8 * q + lcol + e < d.N) se += __expf(acc[i][k][4 * q + e] - mx);
-        }
-        se += __shfl_xor(se, 32, 64);
-        if (lane < 32 && m < d.M && nh < d.N)
-          epi.stats[m * epi.n_stat + (nh >> 7)] = make_float2(mx, se);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 128 + i * 32 + lrow;
-      if (m >= d.M) continue;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (Epi::kReadModifyWrite) {
-          // old values of the block's 16 columns first, all loads in flight
-          float4 old[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * 128 + k * 32 + 8 * q + lcol;
-            old[q] = epi.load4(m, n, d.N);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * 128 + k * 32 + 8 * q + lcol;
-            const float4 v = make_float4(old[q].x + acc[i][k][4 * q + 0],
-                                         old[q].y + acc[i][k][4 * q + 1],
-                                         old[q].z + acc[i][k][4 * q + 2],
-                                         old[q].w + acc[i][k][4 * q + 3]);
-            epi.store4(m, n, d.N, v, split);
-          }
+          for (int c = 0; c < 16; ++c) mx = max3(max3(mx, v[c].x, v[c].y), v[c].z, v[c].w);
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * 128 + k * 32 + 8 * q + lcol;
-            const float4 v = make_float4(acc[i][k][4 * q + 0], acc[i][k][4 * q + 1],
-                                         acc[i][k][4 * q + 2], acc[i][k][4 * q + 3]);
-            epi.store4(m, n, d.N, v, split);
-          }
+          for (int c = 0; c < 16; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (nw + (c >> 2) * 32 + 8 * (c & 3) + lcol + e < d.N) mx = fmaxf(mx, v[c][e]);
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // exp(v - mx) = 2^(v log2(e) - mx log2(e))
+        const float off = mx == -INFINITY ? 0.0f : -mx * kLog2e;
+        float se = 0.0f;
+        if (full) {
+#pragma unroll
+          for (int c = 0; c < 16; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f(fmaf(v[c][e], kLog2e, off));
+        } else if (mx != -INFINITY) {
+#pragma unroll
+          for (int c = 0; c < 16; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (nw + (c >> 2) * 32 + 8 * (c & 3) + lcol + e < d.N)
+                se += __builtin_amdgcn_exp2f(fmaf(v[c][e], kLog2e, off));
+        }
+        se += __shfl_xor(se, 32, 64);
+        if (lane < 32 && m < d.M && nw < d.N)
+          epi.stats[m * epi.n_stat + (nw >> 7)] = make_float2(mx, se);
       }
     }
-  }
+
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      *(LDS_AS f32x4 *)(slab + lrow * kSlabPitch + (c >> 2) * 32 + 8 * (c & 3) + lcol) = v[c];
+    // A wave's LDS operations complete in order, so the reads see the writes;
+    // all sixteen are issued before the first store waits for them.
+    f32x4 rd[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      rd[j] = *(const LDS_AS f32x4 *)(slab + (2 * j + crow) * kSlabPitch + ccol);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (Epi::kReadModifyWrite) {
+        rd[j].x += old[i & 1][j].x;
+        rd[j].y += old[i & 1][j].y;
+        rd[j].z += old[i & 1][j].z;
+        rd[j].w += old[i & 1][j].w;
+      }
+    }
+    int64_t mrow = mw + i * 32 + crow;
+    asm volatile("" : "+v"(mrow));  // row addresses are formed here, per slab
+    if (interior) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) epi.store4_in(mrow + 2 * j, nw + ccol, rd[j], split);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (mrow + 2 * j < d.M)
+          epi.store4(mrow + 2 * j, nw + ccol, d.N,
+                     make_float4(rd[j].x, rd[j].y, rd[j].z, rd[j].w), split);
+    }
+    if constexpr (Epi::kReadModifyWrite) {
+      if constexpr (i + 2 < 4) load_old(i + 2, old[i & 1]);
+    }
+  };
+  do_slab(std::integral_constant<int, 0>{});
+  do_slab(std::integral_constant<int, 1>{});
+  do_slab(std::integral_constant<int, 2>{});
+  do_slab(std::integral_constant<int, 3>{});
 }
 
 inline int cdiv(int64_t a, int64_t b) { return int((a + b - 1) / b); }

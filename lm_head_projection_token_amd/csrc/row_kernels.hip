@@ -217,9 +217,9 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
         B += red[w][4];
       }
     const float l = M + __logf(Ssum);
-    if (HEAD == HEAD_SEL) a.rowval[gr] = s_label - l;  // log p(y)
-    if (HEAD == HEAD_CE) a.rowval[gr] = l - s_label;   // -log p(y)
-    else if (!a.stats) a.rowval[gr] = A - B + Q * l;   // sum_v q log q - q (S - l)
+    if (HEAD == HEAD_SEL) a.rowval[gr] = s_label - l;            // log p(y)
+    if (HEAD == HEAD_CE) a.rowval[gr] = l - s_label;             // -log p(y)
+    if (HEAD == HEAD_KL && !a.stats) a.rowval[gr] = A - B + Q * l;  // sum_v q log q - q (S - l)
     bcast[0] = l;
     bcast[1] = Q;
     bcast[2] = A;
