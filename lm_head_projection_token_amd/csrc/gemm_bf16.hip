@@ -38,10 +38,13 @@
 // contiguous run of that sequence. Which combination keeps the most operand
 // slices in L2 (and shares MALL fills across XCDs) was measured per product
 // on the head shapes (C = 4096, H = 4096, V = 128256):
-//   logits: groups of 16 tile-rows in dispatch order (each XCD keeps two X
-//           panels resident while all XCDs stream the same W panels);
+//   logits: groups of 4 tile-rows, one contiguous run per XCD (each XCD
+//           streams its own share of the W panels, 4 X panels at a time);
 //   dX:     groups of 4 tile-columns in dispatch order;
-//   dW:     groups of 8 tile-rows, one contiguous run per XCD.
+//   dW:     groups of 4 tile-columns, one contiguous run per XCD.
+// Launched in the loss's own sequence (logits and dX alternating over the
+// same W), the orders differ by about 1%; alone, the logits order is ~10%
+// faster than a plain dispatch-order one.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -734,9 +737,9 @@ void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
   d.K = K;
   d.split_len = K;
   d.splits = 1;
-  d.group = 16;       // measured best for the head shapes: see the tile-order note
+  d.group = 4;        // measured best for the head shapes: see the tile-order note
   d.n_first = 0;
-  d.xcd_remap = 0;
+  d.xcd_remap = 1;
   EpiLogits e{S, lds, static_cast<const unsigned short *>(b), inv_tau, stats, n_stat};
   launch<true, true>(d, e, st);
 }
@@ -773,8 +776,8 @@ void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx, flo
   d.K = K;
   d.split_len = K;
   d.splits = 1;
-  d.group = 8;
-  d.n_first = 0;
+  d.group = 4;
+  d.n_first = 1;
   d.xcd_remap = 1;
   EpiDw e{dW, N, accumulate};
   launch<false, false>(d, e, st);
