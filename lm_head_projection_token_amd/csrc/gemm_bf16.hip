@@ -78,7 +78,8 @@ constexpr int kVmcntPrologue = kLoadsPerStage * (NSTAGE - 2);
 // Epilogue slab: 32 rows of the wave's 128 fp32 columns, rows 528 bytes apart.
 constexpr int kSlabPitch = 132;                     // floats
 constexpr int kSlabBytes = 32 * kSlabPitch * 4;     // 16896 per wave
-static_assert(4 * kSlabBytes <= NSTAGE * kStageBytes, "epilogue slabs reuse the stages");
+static_assert(4 * kSlabBytes + BN * 4 <= NSTAGE * kStageBytes,
+              "epilogue slabs and bias table reuse the stages");
 constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
 constexpr unsigned kMaxRecords = 0x7fffffffu;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
@@ -110,7 +111,6 @@ struct OpK {
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
   int kc[4];         // their K offsets within the slice
   unsigned fa[2];    // LDS addresses of the fragment reads (half-step 0 and 1)
-  unsigned fa_hi[2]; // the same + 64 KB (stages past the 16-bit read offset)
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
                                        int64_t nrows_, int wave, int lane, int wr,
@@ -131,7 +131,6 @@ struct OpK {
     for (int h = 0; h < 2; ++h) {
       const int c = 2 * h + (lane >> 5);
       fa[h] = lds_base + unsigned(r * 64 + 16 * (c ^ swz_k(r)));
-      fa_hi[h] = fa[h] + 65536u;
     }
   }
   // Load chunk i of this thread's share of the slice starting at K = k0 into
@@ -149,7 +148,9 @@ struct OpK {
   // block X (rows wr + 32 X ...). The stage and block offsets are immediates.
   template <int OFF, int X, int H>
   __device__ __forceinline__ void read(bf16x8 (&f)[4]) const {
-    const unsigned base = OFF >= 65536 ? fa_hi[H] : fa[H];
+    // the read offset field is 16 bits: whole 64 KB steps go into the base
+    // (loop-invariant, so held in a register)
+    const unsigned base = fa[H] + unsigned(OFF >> 16) * 65536u;
     asm volatile("ds_read_b128 %0, %1 offset:%2"
                  : "=v"(f[X])
                  : "v"(base), "i"(OFF % 65536 + X * 2048));
@@ -162,7 +163,6 @@ struct OpMN {
   int64_t ld, col0;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (k0, col0)
   unsigned fb[4];    // LDS addresses of the transpose reads, block i (half-step 0)
-  unsigned fb_hi[4]; // the same + 64 KB
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t col0_,
                                        int wave, int lane, int wr, unsigned lds_base) {
@@ -184,7 +184,6 @@ struct OpMN {
       const int col = wr + 32 * i + 16 * (G & 1) + 4 * (q & 3);
       const int c = col >> 3, half = (col >> 2) & 1;
       fb[i] = lds_base + unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
-      fb_hi[i] = fb[i] + 65536u;
     }
   }
   // K-rows past kend lie outside the descriptor and read as zero, so no
@@ -202,7 +201,7 @@ struct OpMN {
   template <int OFF, int X, int H>
   __device__ __forceinline__ void read(bf16x8 (&f)[4]) const {
     constexpr int i = X >> 1;
-    const unsigned base = OFF >= 65536 ? fb_hi[i] : fb[i];
+    const unsigned base = fb[i] + unsigned(OFF >> 16) * 65536u;
     i16x4 v;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
                  : "=v"(v)
@@ -388,8 +387,7 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
-  __shared__ __attribute__((aligned(16))) float btab_[Epi::kRowStats ? BN : 1];
-  LDS_AS float *btab = (LDS_AS float *)btab_;
+
   LDS_AS char *lds = (LDS_AS char *)smem;
 
   // ---- tile: optional XCD remap, then grouped order ----
@@ -559,12 +557,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   // back so that one instruction covers two rows x 128 columns, i.e. 512
   // contiguous bytes per row. Rows of the slab sit 528 bytes apart in LDS,
   // which spreads both the writes and the reads over all banks.
-  // The bias of the tile's 256 columns (0 past N) goes to LDS: read per slab,
-  // it is not held in registers across the epilogue.
-  if constexpr (Epi::kRowStats) {
-    if (epi.bias) btab[t] = n0 + t < d.N ? epi.col_bias(n0 + t) : 0.0f;
-  }
   __syncthreads();  // every wave is done reading the staging buffers
+  // The bias of the tile's 256 columns (0 past N) goes to LDS after the four
+  // slabs: read per slab, it is not held in registers across the epilogue.
+  LDS_AS float *btab = (LDS_AS float *)(lds + 4 * kSlabBytes);
+  if constexpr (Epi::kRowStats) {
+    if (epi.bias) {
+      btab[t] = n0 + t < d.N ? epi.col_bias(n0 + t) : 0.0f;
+      __syncthreads();
+    }
+  }
   LDS_AS float *slab = (LDS_AS float *)(lds + wave * kSlabBytes);
   const int lrow = lane & 31;
   const int lcol = 4 * (lane >> 5);
