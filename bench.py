@@ -8,7 +8,8 @@ seeded, and resident in HBM before timing starts.
 Default workload: GRPO selective log-prob with a frozen head, B=8, T=1024
 (BT = 8192 tokens), H = 4096, V = 128256, bf16 -- the head shape and batch
 the frozen lm_head GRPO page times (Details). ``--config 5`` selects the
-trainable KL distillation workload at the same H and V.
+trainable KL distillation workload at the same H and V, ``--config jsd`` the
+Jensen-Shannon head against a teacher with its own H = 4096 projection.
 
 Prints one JSON line. ``roofline`` covers the dominant kernel, timed with
 HIP events on the library's stream over the timed steps; ``cpu_baseline``
@@ -54,16 +55,26 @@ def measured_traffic(case, kind):
 
 
 def gemm_flops(case):
-    """Algorithmic flops of one step: logits and dX GEMMs, plus dW if formed."""
+    """Algorithmic flops of one step: logits and dX GEMMs, plus dW if formed,
+    plus the teacher's logits GEMM for the JSD head."""
     f = 4.0 * case.BT * case.H * case.V
     if case.compute_dW:
         f += 2.0 * case.BT * case.H * case.V
+    if case.head == "jsd":
+        f += 2.0 * case.BT * case.H_teacher * case.V
     return f
 
 
 def kernel_flops(kind, case):
     per = 2.0 * case.BT * case.H * case.V
-    return {"logits": per, "dx": per, "dw": per if case.compute_dW else 0.0}.get(kind, 0.0)
+    return {"logits": per, "dx": per, "dw": per if case.compute_dW else 0.0,
+            "teacher": 2.0 * case.BT * case.H_teacher * case.V}.get(kind, 0.0)
+
+
+def row_bytes_per_valid_row(case):
+    """Algorithmic HBM bytes of the row kernel per valid row: one read of the
+    logits (and of the target or the teacher's logits) and one write of dZ."""
+    return (10 if case.head in ("kl", "jsd") else 6) * case.V
 
 
 def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
@@ -81,6 +92,8 @@ def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
 
     Wd = inp["W"]
     bd = inp["b"]
+    Wt = None if inp["W_teacher"] is None else inp["W_teacher"].double().numpy()
+    bt = None if inp["b_teacher"] is None else inp["b_teacher"].double().numpy()
 
     def run(R):
         rows = np.arange(R)
@@ -93,7 +106,9 @@ def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
             target_rows=None if inp["target"] is None else inp["target"][:R].double().numpy(),
             weights_rows=None if inp["weights"] is None else inp["weights"][:R].double().numpy(),
             reduction=case.reduction, ignore_index=case.ignore_index,
-            temperature=case.temperature, eps=case.eps)
+            temperature=case.temperature, eps=case.eps,
+            Xt_rows=None if inp["X_teacher"] is None else inp["X_teacher"][:R].double().numpy(),
+            W_teacher=Wt, b_teacher=bt)
         return time.perf_counter() - t0
 
     t1 = run(rows_small)
@@ -104,7 +119,8 @@ def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
     return {
         "value": case.BT / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"numpy float64 oracle (sampled_rows: logits, log-softmax, loss terms, "
-                   f"dlogits, dX) timed on the first {rows_small} and {rows_big} token rows "
+                   f"dlogits, dX{', teacher logits' if case.head == 'jsd' else ''}) timed on "
+                   f"the first {rows_small} and {rows_big} token rows "
                    f"({t1:.2f} s, {t2:.2f} s), extrapolated linearly to BT={case.BT}"
                    + ("; the dW GEMM is not in the sample" if case.compute_dW else "")),
     }
@@ -115,7 +131,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", default="3", choices=["2", "3", "4", "5", "jsd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -144,7 +160,7 @@ def main():
     import lm_head_projection_token_amd as fll
     import workloads
 
-    case = workloads.CONFIGS[args.config]
+    case = workloads.JSD_WORKLOAD if args.config == "jsd" else workloads.CONFIGS[int(args.config)]
     inp = workloads.make_inputs(case)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -154,11 +170,13 @@ def main():
 
     X, W, b = d(inp["X"]), d(inp["W"]), d(inp["b"])
     labels, target, weights = d(inp["labels"]), d(inp["target"]), d(inp["weights"])
+    Xt, Wt, bt = d(inp["X_teacher"]), d(inp["W_teacher"]), d(inp["b_teacher"])
     prob = fll.make_problem(case.BT, case.H, case.V, dtype=case.dtype, head=case.head,
                             has_bias=case.has_bias, compute_dW=case.compute_dW,
                             compute_db=case.compute_db, reduction=case.reduction,
                             ignore_index=case.ignore_index, temperature=case.temperature,
-                            eps=case.eps)
+                            eps=case.eps, H_teacher=case.H_teacher,
+                            teacher_has_bias=case.teacher_has_bias)
     plan = fll.fll_plan(prob, 0, args.chunk_rows)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     dX = torch.empty_like(X)
@@ -169,7 +187,8 @@ def main():
 
     def step():
         fll.fll_fwd_bwd(plan, X=X, W=W, b=b, labels=labels, target=target, weights=weights,
-                        dX=dX, dW=dW, db=db, loss=loss, workspace=ws, stream=stream)
+                        dX=dX, dW=dW, db=db, loss=loss, workspace=ws, stream=stream,
+                        X_teacher=Xt, W_teacher=Wt, b_teacher=bt)
 
     for _ in range(args.warmup):
         step()
@@ -201,7 +220,7 @@ def main():
     for kind, (n, tot) in prof.items():
         if n:
             kernels[kind] = {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
-    gemms = [k for k in ("logits", "dx", "dw") if k in kernels]
+    gemms = [k for k in ("logits", "dx", "dw", "teacher") if k in kernels]
     dom = max(gemms, key=lambda k: kernels[k]["ms_per_step"])
     per_launch = kernel_flops(dom, case) / plan.n_chunks
     achieved = per_launch / (kernels[dom]["avg_ms"] / 1e3) / 1e12
@@ -211,7 +230,7 @@ def main():
                 "flops_per_launch": per_launch}
     row = kernels.get("row")
     if row:
-        bytes_per_row = (10 if case.head == "kl" else 6) * case.V
+        bytes_per_row = row_bytes_per_valid_row(case)
         n_valid = case.BT if inp["labels"] is None else int(
             (inp["labels"] != case.ignore_index).sum())
         row_bytes = bytes_per_row * n_valid / plan.n_chunks
@@ -223,7 +242,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": case.dtype, "data": "synthetic",
         "config": {"workload": case.name, "BT": case.BT, "H": case.H, "V": case.V,
-                   "head": case.head, "compute_dW": case.compute_dW,
+                   "head": case.head, **({"H_teacher": case.H_teacher} if case.head == "jsd" else {}), "compute_dW": case.compute_dW,
                    "compute_db": case.compute_db, "chunk_rows": plan.chunk_rows,
                    "n_chunks": plan.n_chunks, "parallelism": "single GPU"},
         "end_to_end_frac_of_bf16_peak": e2e_frac,

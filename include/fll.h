@@ -9,7 +9,7 @@
  *   loss   = g * sum_r w_r * L_r                 (scalar, on the device)
  *   dX     = dZ W,  dW = dZ^T X,  db = sum_r dZ_r (dZ = d loss / d(X W^T + b))
  *
- * with one of two per-row heads:
+ * with one of four per-row heads:
  *
  *   FLL_HEAD_KL:                L_r = sum_v q_rv log(max(q_rv, eps)) - q_rv logP_rv
  *       KL(target || model) against an explicit target distribution q
@@ -18,6 +18,12 @@
  *       the per-token selective log-prob of the GRPO family
  *       [frozen lm_head GRPO page, Summary].
  *   FLL_HEAD_CROSS_ENTROPY:     L_r = -logP_{r, y_r}, weighted by w_r
+ *   FLL_HEAD_JSD:               L_r = 1/2 KL(Pt_r || M_r) + 1/2 KL(P_r || M_r),
+ *       M = (Pt + P) / 2, the Jensen-Shannon divergence between the model and
+ *       a teacher whose distribution Pt comes from its own projection
+ *       Pt = softmax((X_t W_t^T + b_t) / temperature), which takes no gradient
+ *       [FusedLinearKLDivLoss page, Summary: the fused JSD loss whose teacher
+ *       side needs its own projection]
  *
  * The work runs in token chunks, and each chunk's gradient is formed inside
  * the same call (gradient-in-forward), so the BT x V logits are never
@@ -47,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FLL_VERSION 1
+#define FLL_VERSION 2
 
 /* A hipStream_t, passed opaquely. NULL means the null (default) stream. */
 typedef void *fll_stream;
@@ -66,14 +72,15 @@ typedef enum {
 typedef enum {
   FLL_HEAD_KL = 0,
   FLL_HEAD_SELECTIVE_LOGPROB = 1,
-  FLL_HEAD_CROSS_ENTROPY = 2
+  FLL_HEAD_CROSS_ENTROPY = 2,
+  FLL_HEAD_JSD = 3
 } fll_head;
 
 /* Reductions with the semantics of torch.nn.KLDivLoss
  * [FusedLinearKLDivLoss page, Details]. With n = the number of rows whose
  * label is not ignore_index (all rows when labels is NULL):
- *   BATCHMEAN: g = 1/n;  MEAN: g = 1/(n V) for KL, 1/n for the selective
- *   and cross-entropy heads (their tokens are the batch);  SUM: g = 1;
+ *   BATCHMEAN: g = 1/n;  MEAN: g = 1/(n V) for KL and JSD, 1/n for the
+ *   selective and cross-entropy heads (their tokens are the batch);  SUM: g = 1;
  *   n = 0 gives g = 0.
  * NONE is refused with FLL_ERR_UNSUPPORTED: gradient-in-forward needs a
  * scalar loss [FusedLinearKLDivLoss page, Details]. */
@@ -100,8 +107,13 @@ typedef struct {
   int32_t compute_db;   /* 0/1: form db (fp32); needs has_bias               */
   int32_t reduction;    /* fll_reduction                                     */
   int64_t ignore_index; /* label value marking a row as ignored (e.g. -100)  */
-  float temperature;    /* > 0, finite; divides the model logits only        */
+  float temperature;    /* > 0, finite; divides the model logits (and, for
+                           JSD, the teacher's logits)                         */
   float eps;            /* >= 0, finite; KL clamps q inside log(q) only       */
+  int64_t H_teacher;    /* JSD: the teacher's hidden size, >= 8 and a multiple
+                           of 8; every other head: 0                          */
+  int32_t teacher_has_bias; /* JSD: 0/1, b_teacher is given; otherwise 0      */
+  int32_t reserved;     /* 0                                                  */
 } fll_problem;
 
 /* The plan: a value type (nothing to free). Its fields after `p` are the
@@ -120,6 +132,8 @@ typedef struct {
   size_t off_stats;
   size_t off_dx_partial;
   size_t off_scalars;
+  size_t off_teacher;     /* JSD: teacher logits and statistics of a chunk  */
+  size_t off_teacher_stats;
   size_t workspace_bytes; /* bytes the caller must provide                  */
 } fll_plan_t;
 
@@ -129,23 +143,27 @@ typedef struct {
   const void *W;       /* [V x H], dtype                                      */
   const void *b;       /* [V], dtype; NULL iff has_bias == 0                  */
   const int64_t *labels; /* [BT]. SELECTIVE, CROSS_ENTROPY: required, values
-                            in [0, V) or ignore_index. KL: optional row mask
-                            (a row is ignored iff its label == ignore_index). */
+                            in [0, V) or ignore_index. KL, JSD: optional row
+                            mask (a row is ignored iff its label == ignore_index). */
   const float *target; /* KL: [BT x V] fp32 target probabilities, required.
-                          Rows of ignored tokens are never read.              */
+                          Rows of ignored tokens are never read. Other heads:
+                          NULL.                                               */
   const float *weights; /* SELECTIVE, CROSS_ENTROPY: [BT] fp32 per-token
-                           weights (advantages); NULL means all 1. KL: NULL.  */
+                           weights (advantages); NULL means all 1. KL, JSD: NULL. */
   void *dX;            /* [BT x H], dtype: written (every row, ignored = 0)    */
   float *dW;           /* [V x H] fp32: written iff compute_dW, else untouched
                           and may be NULL                                     */
   float *db;           /* [V] fp32: written iff compute_db, else untouched    */
   float *loss;         /* [1] fp32: written                                   */
   float *per_row;      /* optional [BT] fp32: KL_r (KL), log p(y_r)
-                          (SELECTIVE) or -log p(y_r) (CROSS_ENTROPY) before
-                          weighting; 0 on ignored rows                       */
+                          (SELECTIVE), -log p(y_r) (CROSS_ENTROPY) or JS_r
+                          (JSD) before weighting; 0 on ignored rows          */
   void *workspace;     /* >= plan.workspace_bytes, 256-byte aligned; contents
                           are scratch and need no initialisation              */
   size_t workspace_bytes;
+  const void *X_teacher; /* JSD: [BT x H_teacher], dtype, 16-byte aligned; else NULL */
+  const void *W_teacher; /* JSD: [V x H_teacher], dtype, 16-byte aligned; else NULL  */
+  const void *b_teacher; /* JSD: [V], dtype, iff teacher_has_bias; else NULL          */
 } fll_args;
 
 /* Plan a problem: choose the token-chunk size and the workspace layout.
@@ -209,7 +227,8 @@ enum {
   FLL_K_DW = 5,       /* dW GEMM                                        */
   FLL_K_DB = 6,       /* db column sums                                 */
   FLL_K_FINAL = 7,    /* loss reduction                                 */
-  FLL_K_COUNT = 8
+  FLL_K_TEACHER = 8,  /* JSD: teacher logits GEMM                       */
+  FLL_K_COUNT = 9
 };
 
 typedef struct {

@@ -32,8 +32,9 @@ FLL_ERR_HIP = -4
 FLL_HEAD_KL = 0
 FLL_HEAD_SELECTIVE_LOGPROB = 1
 FLL_HEAD_CROSS_ENTROPY = 2
+FLL_HEAD_JSD = 3
 HEADS = {"kl": FLL_HEAD_KL, "selective": FLL_HEAD_SELECTIVE_LOGPROB,
-         "ce": FLL_HEAD_CROSS_ENTROPY}
+         "ce": FLL_HEAD_CROSS_ENTROPY, "jsd": FLL_HEAD_JSD}
 
 FLL_RED_BATCHMEAN, FLL_RED_MEAN, FLL_RED_SUM, FLL_RED_NONE = 0, 1, 2, 3
 REDUCTIONS = {"batchmean": 0, "mean": 1, "sum": 2, "none": 3}
@@ -41,7 +42,8 @@ REDUCTIONS = {"batchmean": 0, "mean": 1, "sum": 2, "none": 3}
 FLL_BF16, FLL_FP32 = 0, 1
 DTYPES = {"bf16": FLL_BF16, "fp32": FLL_FP32}
 
-KERNEL_KINDS = ["prep", "logits", "row", "dx", "dx_reduce", "dw", "db", "final"]
+KERNEL_KINDS = ["prep", "logits", "row", "dx", "dx_reduce", "dw", "db", "final",
+                "teacher"]
 
 
 class FllProblem(ctypes.Structure):
@@ -51,7 +53,8 @@ class FllProblem(ctypes.Structure):
         ("has_bias", ctypes.c_int32), ("compute_dW", ctypes.c_int32),
         ("compute_db", ctypes.c_int32), ("reduction", ctypes.c_int32),
         ("ignore_index", ctypes.c_int64), ("temperature", ctypes.c_float),
-        ("eps", ctypes.c_float),
+        ("eps", ctypes.c_float), ("H_teacher", ctypes.c_int64),
+        ("teacher_has_bias", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -63,6 +66,7 @@ class FllPlan(ctypes.Structure):
         ("stat_tiles", ctypes.c_int64), ("off_logits", ctypes.c_size_t),
         ("off_rowval", ctypes.c_size_t), ("off_stats", ctypes.c_size_t),
         ("off_dx_partial", ctypes.c_size_t), ("off_scalars", ctypes.c_size_t),
+        ("off_teacher", ctypes.c_size_t), ("off_teacher_stats", ctypes.c_size_t),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -75,11 +79,13 @@ class FllArgs(ctypes.Structure):
         ("dW", ctypes.c_void_p), ("db", ctypes.c_void_p),
         ("loss", ctypes.c_void_p), ("per_row", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("X_teacher", ctypes.c_void_p), ("W_teacher", ctypes.c_void_p),
+        ("b_teacher", ctypes.c_void_p),
     ]
 
 
 class FllProfile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 8), ("total_ms", ctypes.c_double * 8)]
+    _fields_ = [("launches", ctypes.c_int64 * 9), ("total_ms", ctypes.c_double * 9)]
 
 
 class FllError(RuntimeError):
@@ -148,13 +154,15 @@ def _check(status: int):
 
 def make_problem(BT, H, V, *, dtype="bf16", head="kl", has_bias=False, compute_dW=False,
                  compute_db=False, reduction="batchmean", ignore_index=-100,
-                 temperature=1.0, eps=1e-10) -> FllProblem:
+                 temperature=1.0, eps=1e-10, H_teacher=0,
+                 teacher_has_bias=False) -> FllProblem:
     return FllProblem(
         BT=BT, H=H, V=V, dtype=DTYPES[dtype] if isinstance(dtype, str) else dtype,
         head=HEADS[head] if isinstance(head, str) else head,
         has_bias=int(has_bias), compute_dW=int(compute_dW), compute_db=int(compute_db),
         reduction=REDUCTIONS[reduction] if isinstance(reduction, str) else reduction,
-        ignore_index=ignore_index, temperature=temperature, eps=eps)
+        ignore_index=ignore_index, temperature=temperature, eps=eps, H_teacher=H_teacher,
+        teacher_has_bias=int(teacher_has_bias), reserved=0)
 
 
 def fll_plan(problem: FllProblem, max_workspace_bytes: int = 0,
@@ -176,7 +184,8 @@ def _ptr(t) -> Optional[int]:
 
 def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weights=None,
                 dX, dW=None, db=None, loss, per_row=None, workspace,
-                workspace_bytes: Optional[int] = None, stream=None) -> None:
+                workspace_bytes: Optional[int] = None, stream=None, X_teacher=None,
+                W_teacher=None, b_teacher=None) -> None:
     """Enqueue one fused forward + backward on ``stream`` (torch stream,
     raw handle int, or None for torch's current stream). Tensors must be
     contiguous device tensors of the dtypes ``include/fll.h`` states."""
@@ -184,7 +193,9 @@ def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weight
 
     for name, t in (("X", X), ("W", W), ("b", b), ("labels", labels), ("target", target),
                     ("weights", weights), ("dX", dX), ("dW", dW), ("db", db),
-                    ("loss", loss), ("per_row", per_row), ("workspace", workspace)):
+                    ("loss", loss), ("per_row", per_row), ("workspace", workspace),
+                    ("X_teacher", X_teacher), ("W_teacher", W_teacher),
+                    ("b_teacher", b_teacher)):
         if isinstance(t, torch.Tensor) and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if workspace_bytes is None:
@@ -193,7 +204,9 @@ def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weight
     args = FllArgs(X=_ptr(X), W=_ptr(W), b=_ptr(b), labels=_ptr(labels),
                    target=_ptr(target), weights=_ptr(weights), dX=_ptr(dX), dW=_ptr(dW),
                    db=_ptr(db), loss=_ptr(loss), per_row=_ptr(per_row),
-                   workspace=_ptr(workspace), workspace_bytes=workspace_bytes)
+                   workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
+                   X_teacher=_ptr(X_teacher), W_teacher=_ptr(W_teacher),
+                   b_teacher=_ptr(b_teacher))
     if stream is None:
         handle = torch.cuda.current_stream().cuda_stream
     elif isinstance(stream, int):
@@ -216,18 +229,21 @@ def fll_profile_read(reset: bool = False) -> dict:
 def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=None,
                        reduction="batchmean", ignore_index=-100, temperature=1.0, eps=1e-10,
                        compute_dW=False, compute_db=False, chunk_rows=0, per_row=False,
-                       workspace=None):
+                       workspace=None, X_teacher=None, W_teacher=None, b_teacher=None):
     """Allocate outputs with torch and run the fused loss. Returns a dict with
-    loss (0-dim fp32 tensor), dX, dW, db and (if asked) per_row."""
+    loss (0-dim fp32 tensor), dX, dW, db and (if asked) per_row. The JSD head
+    takes the teacher's X_teacher [BT, H_t], W_teacher [V, H_t] (+ b_teacher)."""
     import torch
 
     dev = X.device
     BT, H = X.shape
     V = W.shape[0]
     dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}[X.dtype]
+    H_t = X_teacher.shape[1] if X_teacher is not None else 0
     prob = make_problem(BT, H, V, dtype=dtype, head=head, has_bias=b is not None,
                         compute_dW=compute_dW, compute_db=compute_db, reduction=reduction,
-                        ignore_index=ignore_index, temperature=temperature, eps=eps)
+                        ignore_index=ignore_index, temperature=temperature, eps=eps,
+                        H_teacher=H_t, teacher_has_bias=b_teacher is not None)
     plan = fll_plan(prob, 0, chunk_rows)
     if workspace is None or workspace.numel() < plan.workspace_bytes:
         workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
@@ -240,6 +256,7 @@ def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=
     )
     fll_fwd_bwd(plan, X=X, W=W, b=b, labels=labels, target=target, weights=weights,
                 dX=out["dX"], dW=out["dW"], db=out["db"], loss=out["loss"],
-                per_row=out["per_row"], workspace=workspace)
+                per_row=out["per_row"], workspace=workspace, X_teacher=X_teacher,
+                W_teacher=W_teacher, b_teacher=b_teacher)
     out["plan"] = plan
     return out

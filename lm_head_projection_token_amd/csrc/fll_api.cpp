@@ -49,8 +49,19 @@ int check_problem(const fll_problem *p) {
   if (p->dtype != FLL_BF16 && p->dtype != FLL_FP32)
     return fail(FLL_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   if (p->head != FLL_HEAD_KL && p->head != FLL_HEAD_SELECTIVE_LOGPROB &&
-      p->head != FLL_HEAD_CROSS_ENTROPY)
+      p->head != FLL_HEAD_CROSS_ENTROPY && p->head != FLL_HEAD_JSD)
     return fail(FLL_ERR_INVALID_ARG, "unknown head %d", p->head);
+  if (p->head == FLL_HEAD_JSD) {
+    if (p->H_teacher < 8 || p->H_teacher % 8 != 0 || p->H_teacher > (int64_t(1) << 20))
+      return fail(FLL_ERR_INVALID_ARG,
+                  "the JSD head needs H_teacher, a multiple of 8 in [8, 2^20] (got %lld)",
+                  (long long)p->H_teacher);
+    if (p->teacher_has_bias != 0 && p->teacher_has_bias != 1)
+      return fail(FLL_ERR_INVALID_ARG, "flags must be 0 or 1");
+  } else if (p->H_teacher != 0 || p->teacher_has_bias != 0) {
+    return fail(FLL_ERR_INVALID_ARG, "H_teacher and teacher_has_bias are for the JSD head");
+  }
+  if (p->reserved != 0) return fail(FLL_ERR_INVALID_ARG, "reserved must be 0");
   if (p->BT < 0) return fail(FLL_ERR_INVALID_ARG, "BT < 0");
   if (p->V < 1) return fail(FLL_ERR_INVALID_ARG, "V must be >= 1");
   if (p->H < 8 || p->H % 8 != 0)
@@ -93,6 +104,14 @@ void layout(fll_plan_t *pl, int64_t C) {
   if (pl->dx_splits > 1) off = align256(off + size_t(pl->dx_splits) * C * p.H * 4);
   pl->off_scalars = off;
   off = align256(off + sizeof(fll::DevScalars));
+  // JSD: the teacher's logits of the chunk and their row statistics
+  pl->off_teacher = off;
+  pl->off_teacher_stats = off;
+  if (p.head == FLL_HEAD_JSD) {
+    off = align256(off + size_t(C) * size_t(pl->s_pitch) * 4);
+    pl->off_teacher_stats = off;
+    off = align256(off + size_t(C) * size_t(pl->stat_tiles) * 8);
+  }
   pl->workspace_bytes = off;
 }
 
@@ -161,16 +180,31 @@ int check_args(const fll_plan_t *pl, const fll_args *a) {
   if (!a->X || !a->W || !a->dX) return fail(FLL_ERR_INVALID_ARG, "X, W and dX are required");
   if (!aligned(a->X, 16) || !aligned(a->W, 16) || !aligned(a->dX, 16))
     return fail(FLL_ERR_INVALID_ARG, "X, W and dX must be 16-byte aligned");
-  if (p.head != FLL_HEAD_KL) {
+  if (p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY) {
     if (!a->labels)
       return fail(FLL_ERR_INVALID_ARG, "the selective and cross-entropy heads need labels");
     if (a->target)
       return fail(FLL_ERR_INVALID_ARG, "target given for a label head");
-  } else {
+  } else if (p.head == FLL_HEAD_KL) {
     if (!a->target) return fail(FLL_ERR_INVALID_ARG, "the KL head needs a target");
     if (a->weights) return fail(FLL_ERR_INVALID_ARG, "weights given for the KL head");
     if (!aligned(a->target, 4)) return fail(FLL_ERR_INVALID_ARG, "target misaligned");
+  } else {
+    if (a->target || a->weights)
+      return fail(FLL_ERR_INVALID_ARG, "the JSD head takes no target and no weights");
+    if (!a->X_teacher || !a->W_teacher)
+      return fail(FLL_ERR_INVALID_ARG, "the JSD head needs X_teacher and W_teacher");
+    if (!aligned(a->X_teacher, 16) || !aligned(a->W_teacher, 16))
+      return fail(FLL_ERR_INVALID_ARG, "X_teacher and W_teacher must be 16-byte aligned");
+    if (p.teacher_has_bias && !a->b_teacher)
+      return fail(FLL_ERR_INVALID_ARG, "teacher_has_bias but b_teacher is NULL");
+    if (p.teacher_has_bias && !aligned(a->b_teacher, esz))
+      return fail(FLL_ERR_INVALID_ARG, "b_teacher misaligned");
   }
+  if (p.head != FLL_HEAD_JSD && (a->X_teacher || a->W_teacher || a->b_teacher))
+    return fail(FLL_ERR_INVALID_ARG, "teacher inputs are for the JSD head");
+  if (p.head == FLL_HEAD_JSD && !p.teacher_has_bias && a->b_teacher)
+    return fail(FLL_ERR_INVALID_ARG, "b_teacher given but teacher_has_bias is 0");
   if (a->labels && !aligned(a->labels, 8)) return fail(FLL_ERR_INVALID_ARG, "labels misaligned");
   if (a->weights && !aligned(a->weights, 4)) return fail(FLL_ERR_INVALID_ARG, "weights misaligned");
   if (a->per_row && !aligned(a->per_row, 4)) return fail(FLL_ERR_INVALID_ARG, "per_row misaligned");
@@ -268,6 +302,11 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   float *partial = reinterpret_cast<float *>(ws + plan->off_dx_partial);
   float2 *stats = plan->stat_tiles ? reinterpret_cast<float2 *>(ws + plan->off_stats) : nullptr;
   auto *sc = reinterpret_cast<fll::DevScalars *>(ws + plan->off_scalars);
+  const bool jsd = p.head == FLL_HEAD_JSD;
+  float *T = jsd ? reinterpret_cast<float *>(ws + plan->off_teacher) : nullptr;
+  float2 *stats_t = jsd && plan->stat_tiles
+                        ? reinterpret_cast<float2 *>(ws + plan->off_teacher_stats)
+                        : nullptr;
   const bool bf16 = p.dtype == FLL_BF16;
   const size_t esz = bf16 ? 2 : 4;
   const float inv_tau = 1.0f / p.temperature;
@@ -291,6 +330,22 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     const int64_t rows = std::min<int64_t>(C, p.BT - r0);
     const char *Xc = static_cast<const char *>(a.X) + size_t(r0) * p.H * esz;
     char *dXc = static_cast<char *>(a.dX) + size_t(r0) * p.H * esz;
+    if (jsd) {
+      // the teacher's own projection: T = (X_t W_t^T + b_t) / tau, with its
+      // row statistics [FusedLinearKLDivLoss page, Summary]
+      const char *Xtc = static_cast<const char *>(a.X_teacher) + size_t(r0) * p.H_teacher * esz;
+      Probe pr(FLL_K_TEACHER, s);
+      if (bf16)
+        fll::launch_logits_bf16(Xtc, p.H_teacher, a.W_teacher, p.H_teacher, a.b_teacher,
+                                inv_tau, T, plan->s_pitch, stats_t, plan->stat_tiles, rows,
+                                p.V, p.H_teacher, s);
+      else
+        fll::launch_logits_f32(reinterpret_cast<const float *>(Xtc), p.H_teacher,
+                               static_cast<const float *>(a.W_teacher), p.H_teacher,
+                               static_cast<const float *>(a.b_teacher), inv_tau, T,
+                               plan->s_pitch, rows, p.V, p.H_teacher, s);
+    }
+    if ((st = hip_check("teacher logits GEMM"))) return st;
     {
       Probe pr(FLL_K_LOGITS, s);
       if (bf16)
@@ -322,6 +377,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       ra.rowval = rowval;
       ra.stats = stats;
       ra.n_stat = plan->stat_tiles;
+      ra.T = T;
+      ra.stats_t = stats_t;
       Probe pr(FLL_K_ROW, s);
       fll::launch_row(ra, s);
     }
@@ -362,8 +419,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   }
   {
     Probe pr(FLL_K_FINAL, s);
-    fll::launch_finalize(rowval, p.head != FLL_HEAD_KL ? a.weights : nullptr, p.BT, sc,
-                         a.loss, s);
+    const bool weighted = p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY;
+    fll::launch_finalize(rowval, weighted ? a.weights : nullptr, p.BT, sc, a.loss, s);
   }
   return hip_check("loss reduction");
 }

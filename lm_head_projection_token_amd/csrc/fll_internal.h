@@ -83,6 +83,8 @@ struct RowArgs {
   float *rowval;          // global [BT]
   const float2 *stats;    // per-(row, 128-column block) (max, sum exp) or null
   int64_t n_stat;         // blocks per row
+  const float *T;         // JSD: the chunk's teacher logits (pitch s_pitch) or null
+  const float2 *stats_t;  // JSD: the teacher's block statistics or null
 };
 void launch_row(const RowArgs &a, hipStream_t st);
 

@@ -24,6 +24,7 @@ constexpr int kStrip = kRowThreads * kUnroll;  // float4 groups per strip
 constexpr int HEAD_KL = 0;
 constexpr int HEAD_SEL = 1;
 constexpr int HEAD_CE = 2;  // the selective head with the opposite sign
+constexpr int HEAD_JSD = 3;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -299,6 +300,197 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   if (a.dz_bf16) zero_pad(Zb, V, tid);
 }
 
+// Jensen-Shannon head [FusedLinearKLDivLoss page, Summary: the fused JSD
+// loss, teacher side with its own projection]. One workgroup per token row.
+// With lp = T - lse(T) (teacher), lq = S - lse(S) (model), p = e^lp,
+// q = e^lq and lm = log((p + q) / 2):
+//   JS_r = 1/2 sum_v p (lp - lm) + 1/2 sum_v q (lq - lm)
+//   dS_v = g q_v (1/2 (lq_v - lm_v) - 1/2 sum_u q_u (lq_u - lm_u))
+// (the derivative of JS in q_v is 1/2 (lq_v - lm_v); the softmax Jacobian
+// subtracts its q-weighted mean). A first pass forms both sums — the second
+// enters every dS_v — and a second pass writes dZ = dS / tau in place over S.
+// lm is formed in the log domain, lm = max(lp, lq) + log((1 + e^-|lp - lq|) / 2),
+// so no probability that underflows can make a term undefined.
+struct JsdTerms {
+  float q;        // model probability
+  float gq;       // lq - lm
+  float tp, tq;   // p (lp - lm), q (lq - lm)
+};
+__device__ __forceinline__ JsdTerms jsd_terms(float s, float t, float lse_s, float lse_t) {
+  const float lq = s - lse_s, lp = t - lse_t;
+  const float d = lp - lq;
+  const float r = __expf(-fabsf(d));           // e^-|lp - lq|, in (0, 1]
+  const float big = __expf(fmaxf(lp, lq));     // the larger of p and q
+  const float l1 = __logf(0.5f + 0.5f * r);    // lm - max(lp, lq), in [-log 2, 0]
+  const float p = d >= 0.f ? big : big * r;
+  const float q = d >= 0.f ? big * r : big;
+  const float gp = (d >= 0.f ? 0.f : d) - l1;  // lp - lm
+  const float gq = (d >= 0.f ? -d : 0.f) - l1; // lq - lm
+  return JsdTerms{q, gq, p * gp, q * gq};
+}
+
+__global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
+  __shared__ float red[kRowWaves][8];
+  __shared__ float bcast[8];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t lr = blockIdx.x;
+  const int64_t gr = a.row0 + lr;
+  const int64_t V = a.V;
+  float *Srow = a.S + lr * a.s_pitch;
+  const float *Trow = a.T + lr * a.s_pitch;
+  unsigned short *Zb = reinterpret_cast<unsigned short *>(Srow);  // bf16 dZ
+  const int64_t ngroups = (V + 3) / 4;
+
+  const bool valid = !a.labels || a.labels[gr] != a.ignore_index;
+  if (!valid) {
+    for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+      const int64_t e = 4 * g;
+      for (int i = 0; i < 4; ++i)
+        if (e + i < V) {
+          if (a.dz_bf16) Zb[e + i] = 0;
+          else Srow[e + i] = 0.0f;
+        }
+    }
+    if (tid == 0) a.rowval[gr] = 0.0f;
+    if (a.dz_bf16) zero_pad(Zb, V, tid);
+    return;
+  }
+
+  // ---- log-sum-exp of both rows: from the GEMMs' block statistics, or a pass
+  float ms = -INFINITY, ss = 0.0f, mt = -INFINITY, st = 0.0f;
+  if (a.stats) {
+    const float2 *sa = a.stats + lr * a.n_stat;
+    const float2 *sb = a.stats_t + lr * a.n_stat;
+    for (int64_t t = tid; t < a.n_stat; t += kRowThreads) {
+      const float2 x = sa[t], y = sb[t];
+      lse_merge(ms, ss, x.x, x.y);
+      lse_merge(mt, st, y.x, y.y);
+    }
+  } else {
+    for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+      const Load4 x = load_group(Srow, g, V, true), y = load_group(Trow, g, V, true);
+      const int64_t e = 4 * g;
+      float mx = -INFINITY, my = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e + i < V) {
+          mx = fmaxf(mx, x.v[i]);
+          my = fmaxf(my, y.v[i]);
+        }
+      float sx = 0.0f, sy = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e + i < V) {
+          sx += __expf(x.v[i] - mx);
+          sy += __expf(y.v[i] - my);
+        }
+      lse_merge(ms, ss, mx, sx);
+      lse_merge(mt, st, my, sy);
+    }
+  }
+  {
+    const float wms = wave_max(ms), wmt = wave_max(mt);
+    const float wss = wave_sum(ms == -INFINITY ? 0.0f : ss * __expf(ms - wms));
+    const float wst = wave_sum(mt == -INFINITY ? 0.0f : st * __expf(mt - wmt));
+    if (lane == 0) {
+      red[wave][0] = wms;
+      red[wave][1] = wss;
+      red[wave][2] = wmt;
+      red[wave][3] = wst;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m1 = red[0][0], s1 = red[0][1], m2 = red[0][2], s2 = red[0][3];
+    for (int w = 1; w < kRowWaves; ++w) {
+      lse_merge(m1, s1, red[w][0], red[w][1]);
+      lse_merge(m2, s2, red[w][2], red[w][3]);
+    }
+    bcast[0] = m1 + __logf(s1);
+    bcast[1] = m2 + __logf(s2);
+  }
+  __syncthreads();
+  const float lse_s = bcast[0], lse_t = bcast[1];
+
+  // ---- pass 1: both halves of the divergence
+  float A = 0.0f, B = 0.0f;
+  for (int64_t g = tid; g < ngroups; g += kRowThreads) {
+    const Load4 x = load_group(Srow, g, V, true), y = load_group(Trow, g, V, true);
+    const int64_t e = 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e + i < V) {
+        const JsdTerms j = jsd_terms(x.v[i], y.v[i], lse_s, lse_t);
+        A += j.tp;
+        B += j.tq;
+      }
+  }
+  A = wave_sum(A);
+  B = wave_sum(B);
+  if (lane == 0) {
+    red[wave][4] = A;
+    red[wave][5] = B;
+  }
+  __syncthreads();
+  float Ar = 0.0f, Br = 0.0f;
+  for (int w = 0; w < kRowWaves; ++w) {
+    Ar += red[w][4];
+    Br += red[w][5];
+  }
+  if (tid == 0) a.rowval[gr] = 0.5f * (Ar + Br);
+  const float coef = a.sc->g * a.inv_tau;  // dZ = g (dJS/dS) / tau
+  const float half_b = 0.5f * Br;
+
+  // ---- pass 2: dZ in place, strip by strip (every load of a strip lands
+  // before its barrier, and the bf16 dZ of element v only covers float slots
+  // of elements < v)
+  for (int64_t base = 0; base < ngroups; base += kStrip) {
+    Load4 xs[kUnroll], ys[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = base + u * kRowThreads + tid;
+      if (g < ngroups) {
+        xs[u] = load_group(Srow, g, V, true);
+        ys[u] = load_group(Trow, g, V, true);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = base + u * kRowThreads + tid;
+      if (g >= ngroups) continue;
+      const int64_t e = 4 * g;
+      float d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const JsdTerms j = jsd_terms(xs[u].v[i], ys[u].v[i], lse_s, lse_t);
+        d[i] = coef * j.q * (0.5f * j.gq - half_b);
+      }
+      if (a.dz_bf16) {
+        if (e + 4 <= V) {
+          uint2 pk;
+          pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
+          pk.y = (unsigned)f2bf(d[2]) | ((unsigned)f2bf(d[3]) << 16);
+          *reinterpret_cast<uint2 *>(Zb + e) = pk;
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (e + i < V) Zb[e + i] = f2bf(d[i]);
+        }
+      } else {
+        if (e + 4 <= V) {
+          *reinterpret_cast<float4 *>(Srow + e) = make_float4(d[0], d[1], d[2], d[3]);
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (e + i < V) Srow[e + i] = d[i];
+        }
+      }
+    }
+  }
+  if (a.dz_bf16) zero_pad(Zb, V, tid);
+}
+
 __global__ __launch_bounds__(1024) void prep_kernel(const int64_t *labels, int64_t BT,
                                                     int64_t ignore_index, int head,
                                                     int reduction, int64_t V,
@@ -321,7 +513,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int64_t *labels, int64
     double g;
     if (nv == 0) g = 0.0;
     else if (reduction == 2) g = 1.0;                       // sum
-    else if (reduction == 1 && head == 0) g = 1.0 / (double(nv) * double(V));  // KL mean
+    else if (reduction == 1 && (head == 0 || head == 3))
+      g = 1.0 / (double(nv) * double(V));                   // KL and JSD mean
     else g = 1.0 / double(nv);                              // batchmean; selective mean
     sc->n_valid = nv;
     sc->g = float(g);
@@ -427,8 +620,10 @@ void launch_row(const RowArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(row_kernel<HEAD_KL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
   else if (a.head == HEAD_SEL)
     hipLaunchKernelGGL(row_kernel<HEAD_SEL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
-  else
+  else if (a.head == HEAD_CE)
     hipLaunchKernelGGL(row_kernel<HEAD_CE>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(jsd_row_kernel, dim3(a.rows), dim3(kRowThreads), 0, st, a);
 }
 
 void launch_colsum(const void *dZ, int dz_bf16, int64_t ldz, int64_t rows, int64_t V,

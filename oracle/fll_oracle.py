@@ -22,10 +22,13 @@ W [V, H] (+ b [V]):
 
 1. logits Z = X W^T + b, tempered S = Z / tau (model side only).
 2. log-softmax over the vocabulary: logP = S - lse(S).
-3. the per-row term of one of three heads:
+3. the per-row term of one of four heads:
    KL:        L_r = sum_v q_rv * log(max(q_rv, eps)) - q_rv * logP_rv
    SELECTIVE: L_r = logP_{r, y_r}   (weighted by the advantage w_r)
    CE:        L_r = -logP_{r, y_r}  (cross-entropy: KL against a one-hot target)
+   JSD:       L_r = 1/2 KL(Pt_r || M_r) + 1/2 KL(P_r || M_r), M = (Pt + P) / 2,
+              Pt = softmax of a teacher's own tempered logits
+              (X_t W_t^T + b_t) / tau, the teacher taking no gradient
 4. loss = g * sum_r w_r L_r with g from the reduction and the count of rows
    whose label is not ``ignore_index``.
 5. the exact gradient: dS = d loss / d S, dZ = dS / tau, then
@@ -36,7 +39,9 @@ KL direction is KL(target || model); eps clamps q inside the log only;
 the temperature divides the model logits only, with no tau^2 factor;
 ignored rows leave the batch (denominators count valid rows only);
 the selective head's loss is the advantage-weighted mean of log p(label),
-not negated; "mean" and "batchmean" coincide for the selective head.
+not negated; "mean" and "batchmean" coincide for the selective head;
+the JSD head is the symmetric Jensen-Shannon divergence in natural log, the
+temperature dividing both the teacher's and the student's logits.
 
 Parity status: every function below is pinned by the CPU tests against
 closed forms, invariants, torch library routines in float64 and central
@@ -52,6 +57,7 @@ import numpy as np
 HEAD_KL = "kl"
 HEAD_SELECTIVE = "selective"
 HEAD_CE = "ce"
+HEAD_JSD = "jsd"
 REDUCTIONS = ("batchmean", "mean", "sum")
 
 
@@ -113,6 +119,30 @@ def kl_rows(logP, target, valid, eps):
     return L
 
 
+def jsd_rows(logP, teacher, valid):
+    """Per-row Jensen-Shannon divergence between the teacher distribution
+    Pt (``teacher``, probabilities) and the model P = exp(logP):
+
+        JS_r = 1/2 sum_v Pt log(Pt / M) + 1/2 sum_v P log(P / M),  M = (Pt + P) / 2,
+
+    natural log, a zero probability contributing 0. FusedLinearKLDivLoss
+    page, Summary: the fused JSD loss whose teacher side has its own
+    projection (the divergence itself is not printed there; the symmetric
+    Jensen-Shannon divergence is the plain reading). Ignored rows give 0.
+    """
+    L = np.zeros(logP.shape[0])
+    r = np.nonzero(valid)[0]
+    if r.size:
+        Pt = _f64(teacher)[r]
+        P = np.exp(logP[r])
+        M = 0.5 * (Pt + P)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            tt = np.where(Pt > 0, Pt * np.log(Pt / M), 0.0)
+            tp = np.where(P > 0, P * np.log(P / M), 0.0)
+        L[r] = 0.5 * (tt.sum(axis=1) + tp.sum(axis=1))
+    return L
+
+
 def ce_rows(logP, labels, valid):
     """Per-row cross-entropy -log p(y_r): the KL head with a one-hot target
     (q log q vanishes), the fused linear cross-entropy head the
@@ -143,8 +173,9 @@ def reduction_scale(head, reduction, n_valid, V):
     the semantics of ``torch.nn.KLDivLoss`` (batchmean divides by the batch,
     mean by the element count, sum by 1); ``"none"`` is refused because
     gradient-in-forward needs a scalar loss. With ignored rows the batch is the
-    valid rows. For the selective and cross-entropy heads the tokens are the
-    batch, so mean and batchmean both divide by the valid-token count (the
+    valid rows; the JSD head, a divergence between distributions like KL,
+    takes KL's semantics. For the selective and cross-entropy heads the
+    tokens are the batch, so mean and batchmean both divide by the valid-token count (the
     ``torch.nn.functional.cross_entropy`` mean with ``ignore_index``). No valid
     row gives g = 0.
     """
@@ -154,7 +185,7 @@ def reduction_scale(head, reduction, n_valid, V):
         return 0.0
     if reduction == "sum":
         return 1.0
-    if reduction == "mean" and head == HEAD_KL:
+    if reduction == "mean" and head in (HEAD_KL, HEAD_JSD):
         return 1.0 / (n_valid * V)
     return 1.0 / n_valid
 
@@ -174,9 +205,15 @@ def dlogits(head, logP, target, labels, w, valid, g, temperature):
       KL:        dS_r = g * (Q_r * P_r - q_r),   Q_r = sum_v q_rv
       SELECTIVE: dS_r = g * w_r * (onehot(y_r) - P_r)
       CE:        dS_r = g * w_r * (P_r - onehot(y_r))
+      JSD:       dS_r = g * P_r * (G_r - sum_v P_rv G_rv),  G = 1/2 log(P / M)
     and dZ = dS / tau. Ignored rows are 0. This is the log-softmax backward
     the FusedLinearKLDivLoss page (Details) computes in place on the saved
     log-probs; Q_r keeps it exact even when a target row does not sum to 1.
+    For JSD (``target`` = the teacher probabilities Pt, M = (Pt + P) / 2):
+    d JS / dP_v = 1/2 log(P_v / M_v) (the Pt / M and P / M terms of the
+    derivative of M cancel to a constant that the softmax Jacobian removes),
+    then the softmax Jacobian gives P_v (G_v - sum_u P_u G_u); G_v is taken
+    as 0 where P_v = 0, its limit in the product.
     """
     BT, V = logP.shape
     dS = np.zeros((BT, V))
@@ -187,6 +224,12 @@ def dlogits(head, logP, target, labels, w, valid, g, temperature):
             q = _f64(target)[r]
             Q = q.sum(axis=1, keepdims=True)
             dS[r] = g * (Q * P - q)
+        elif head == HEAD_JSD:
+            Pt = _f64(target)[r]
+            M = 0.5 * (Pt + P)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                G = np.where(P > 0, 0.5 * np.log(P / M), 0.0)
+            dS[r] = g * P * (G - (P * G).sum(axis=1, keepdims=True))
         else:
             y = np.asarray(labels)[r]
             onehot = np.zeros_like(P)
@@ -196,9 +239,18 @@ def dlogits(head, logP, target, labels, w, valid, g, temperature):
     return dS / float(temperature)
 
 
+def teacher_probs(X_teacher, W_teacher, b_teacher, temperature):
+    """The JSD head's teacher distribution: softmax of the teacher's own
+    tempered logits (X_t W_t^T + b_t) / tau (FusedLinearKLDivLoss page,
+    Summary: the JSD teacher side needs its own projection)."""
+    logPt, _ = log_softmax(logits(X_teacher, W_teacher, b_teacher, temperature))
+    return np.exp(logPt)
+
+
 def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
             reduction="batchmean", ignore_index=-100, temperature=1.0,
-            eps=1e-10, compute_dW=True, compute_db=True):
+            eps=1e-10, compute_dW=True, compute_db=True, X_teacher=None,
+            W_teacher=None, b_teacher=None):
     """Loss and gradients of the fused lm_head loss, fully materialised.
 
     The chunked gradient-in-forward structure (FusedLinearKLDivLoss page,
@@ -208,10 +260,12 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
     autograd asks for; LoRA normalization page, Key Changes: COMPUTE_DW and
     COMPUTE_DB prune weight and bias gradients independently).
 
-    Returns a dict with loss (float), per_row [BT] (KL_r, log p(y_r) or
-    -log p(y_r); 0 on ignored rows), dX [BT, H], dW [V, H] or None, db [V] or None, n_valid, g.
+    Returns a dict with loss (float), per_row [BT] (KL_r, log p(y_r),
+    -log p(y_r) or JS_r; 0 on ignored rows), dX [BT, H], dW [V, H] or None,
+    db [V] or None, n_valid, g. The JSD head takes the teacher's X_teacher
+    [BT, H_t], W_teacher [V, H_t] (+ b_teacher [V]) and no ``target``.
     """
-    if head not in (HEAD_KL, HEAD_SELECTIVE, HEAD_CE):
+    if head not in (HEAD_KL, HEAD_SELECTIVE, HEAD_CE, HEAD_JSD):
         raise ValueError(f"unknown head {head!r}")
     if not (temperature > 0 and np.isfinite(temperature)):
         raise ValueError("temperature must be positive and finite")
@@ -231,6 +285,11 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
         if target is None:
             raise ValueError("the KL head needs a target distribution")
         L = kl_rows(logP, target, valid, eps)
+    elif head == HEAD_JSD:
+        if X_teacher is None or W_teacher is None or target is not None:
+            raise ValueError("the JSD head needs a teacher projection and no target")
+        target = teacher_probs(X_teacher, W_teacher, b_teacher, temperature)
+        L = jsd_rows(logP, target, valid)
     else:
         if labels is None:
             raise ValueError("the selective and cross-entropy heads need labels")
@@ -250,7 +309,8 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
 
 def sampled_rows(X_rows, W, b=None, *, head, n_valid, labels_rows=None,
                  target_rows=None, weights_rows=None, reduction="batchmean",
-                 ignore_index=-100, temperature=1.0, eps=1e-10):
+                 ignore_index=-100, temperature=1.0, eps=1e-10,
+                 Xt_rows=None, W_teacher=None, b_teacher=None):
     """The same definition restricted to a subset of rows.
 
     Every step above except the final reduction is row-local, so for a subset
@@ -272,6 +332,9 @@ def sampled_rows(X_rows, W, b=None, *, head, n_valid, labels_rows=None,
     logP, _ = log_softmax(S)
     if head == HEAD_KL:
         L = kl_rows(logP, target_rows, valid, eps)
+    elif head == HEAD_JSD:
+        target_rows = teacher_probs(Xt_rows, W_teacher, b_teacher, temperature)
+        L = jsd_rows(logP, target_rows, valid)
     elif head == HEAD_CE:
         L = ce_rows(logP, labels_rows, valid)
     else:

@@ -26,6 +26,12 @@ CASES = {
     "selective_fp32_small": workloads.small_case(
         BT=10, H=8, V=33, dtype="fp32", head="selective", reduction="mean",
         x_std=1.0, w_std=0.5, seed=8),
+    # Jensen-Shannon head, bf16 inputs, teacher of another hidden size with a
+    # bias, trainable student head, ignored rows.
+    "jsd_bf16_small": workloads.small_case(
+        BT=12, H=16, V=40, dtype="bf16", head="jsd", has_bias=True, compute_dW=True,
+        compute_db=True, H_teacher=24, teacher_has_bias=True, teacher_w_std=0.3,
+        temperature=2.0, ignore_frac=0.25, w_std=0.3, seed=10),
 }
 
 
@@ -41,7 +47,9 @@ def run_case(case):
         target=np_(inp["target"]), weights=np_(inp["weights"]),
         reduction=case.reduction, ignore_index=case.ignore_index,
         temperature=case.temperature, eps=case.eps,
-        compute_dW=case.compute_dW, compute_db=case.compute_db)
+        compute_dW=case.compute_dW, compute_db=case.compute_db,
+        X_teacher=np_(inp["X_teacher"]), W_teacher=np_(inp["W_teacher"]),
+        b_teacher=np_(inp["b_teacher"]))
     rec = dict(loss=out["loss"], per_row=out["per_row"].tolist(),
                n_valid=out["n_valid"], dX_row0=out["dX"][0].tolist(),
                dX_sum=float(out["dX"].sum()))

@@ -33,7 +33,9 @@ def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0"):
         labels=dev(inp["labels"]), target=dev(inp["target"]), weights=dev(inp["weights"]),
         reduction=case.reduction, ignore_index=case.ignore_index,
         temperature=case.temperature, eps=case.eps, compute_dW=case.compute_dW,
-        compute_db=case.compute_db, chunk_rows=chunk_rows, per_row=per_row)
+        compute_db=case.compute_db, chunk_rows=chunk_rows, per_row=per_row,
+        X_teacher=dev(inp.get("X_teacher")), W_teacher=dev(inp.get("W_teacher")),
+        b_teacher=dev(inp.get("b_teacher")))
     torch.cuda.synchronize()
     return out
 
@@ -47,7 +49,8 @@ def run_oracle(inp, case):
         target=to_np(inp["target"]), weights=to_np(inp["weights"]),
         reduction=case.reduction, ignore_index=case.ignore_index,
         temperature=case.temperature, eps=case.eps, compute_dW=case.compute_dW,
-        compute_db=case.compute_db)
+        compute_db=case.compute_db, X_teacher=to_np(inp.get("X_teacher")),
+        W_teacher=to_np(inp.get("W_teacher")), b_teacher=to_np(inp.get("b_teacher")))
 
 
 def check_loss(gpu_loss: float, ref: float, dtype: str, what="loss"):

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(fll.LIB_PATH)
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert fll.fll_version() == 1
+    assert fll.fll_version() == 2
     out = subprocess.run(["nm", "-D", "--defined-only", fll.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fll_\w+)", out))
@@ -149,6 +149,11 @@ def test_plan_empty_batch():
     (dict(dtype=5), fll.FLL_ERR_INVALID_ARG),
     (dict(head=9), fll.FLL_ERR_INVALID_ARG),
     (dict(compute_db=True, has_bias=False), fll.FLL_ERR_INVALID_ARG),
+    (dict(head="jsd"), fll.FLL_ERR_INVALID_ARG),                  # no H_teacher
+    (dict(head="jsd", H_teacher=100), fll.FLL_ERR_INVALID_ARG),   # not a multiple of 8
+    (dict(head="jsd", H_teacher=4096, teacher_has_bias=2), fll.FLL_ERR_INVALID_ARG),
+    (dict(H_teacher=4096), fll.FLL_ERR_INVALID_ARG),              # teacher for another head
+    (dict(teacher_has_bias=True), fll.FLL_ERR_INVALID_ARG),
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(fll.FllError) as e:
@@ -215,6 +220,38 @@ def test_fwd_bwd_rejects_kl_trainable(over, status):
     base = dict(labels=None, weights=None, target=8 * A, b=9 * A, dW=10 * A, db=11 * A)
     base.update(over)
     assert _call(plan, _args(plan, **base)) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X_teacher=None), fll.FLL_ERR_INVALID_ARG),
+    (dict(W_teacher=None), fll.FLL_ERR_INVALID_ARG),
+    (dict(X_teacher=12 * A + 8), fll.FLL_ERR_INVALID_ARG),
+    (dict(b_teacher=None), fll.FLL_ERR_INVALID_ARG),
+    (dict(target=8 * A), fll.FLL_ERR_INVALID_ARG),
+    (dict(weights=4 * A), fll.FLL_ERR_INVALID_ARG),
+])
+def test_fwd_bwd_rejects_jsd(over, status):
+    plan = fll.fll_plan(_prob(BT=512, H=64, V=1000, head="jsd", H_teacher=96,
+                              teacher_has_bias=True))
+    base = dict(labels=None, weights=None, X_teacher=12 * A, W_teacher=13 * A,
+                b_teacher=14 * A)
+    base.update(over)
+    assert _call(plan, _args(plan, **base)) == status
+
+
+def test_fwd_bwd_rejects_teacher_inputs_for_other_heads():
+    plan = fll.fll_plan(_prob(BT=512, H=64, V=1000))
+    assert _call(plan, _args(plan, X_teacher=12 * A)) == fll.FLL_ERR_INVALID_ARG
+
+
+def test_plan_jsd_adds_the_teacher_chunk():
+    # the teacher's logits chunk and statistics come on top of the student's
+    a = fll.fll_plan(_prob(head="kl"))
+    j = fll.fll_plan(_prob(head="jsd", H_teacher=4096))
+    assert j.chunk_rows == a.chunk_rows
+    extra = j.workspace_bytes - a.workspace_bytes
+    assert extra >= j.chunk_rows * j.s_pitch * 4 + j.chunk_rows * j.stat_tiles * 8
+    assert j.off_teacher_stats >= j.off_teacher + j.chunk_rows * j.s_pitch * 4
 
 
 def test_fwd_bwd_rejects_edited_plan():

@@ -43,11 +43,12 @@ def test_cfg2_full():
 # V=128256 GRPO workload, with a trainable head (beyond the five workloads).
 CE_FULL = workloads.CONFIGS[3].replace(name="ce-bf16-trainable-B8T1024-V128256", head="ce",
                                        compute_dW=True, ignore_frac=0.05, seed=6)
+EXTRA = {"ce": CE_FULL, "jsd": workloads.JSD_WORKLOAD}
 
 
-@pytest.mark.parametrize("cfg", [3, 4, 5, "ce"])
+@pytest.mark.parametrize("cfg", [3, 4, 5, "ce", "jsd"])
 def test_full_config_sampled(cfg):
-    case = CE_FULL if cfg == "ce" else workloads.CONFIGS[cfg]
+    case = EXTRA[cfg] if cfg in EXTRA else workloads.CONFIGS[cfg]
     print(f"[cfg{cfg}] {case}", flush=True)
     inp = H.make(case)
     out = H.run_gpu(inp, case)
@@ -61,7 +62,9 @@ def test_full_config_sampled(cfg):
         target_rows=None if inp["target"] is None else H.to_np(inp["target"][rows]),
         weights_rows=None if inp["weights"] is None else H.to_np(inp["weights"][rows]),
         reduction=case.reduction, ignore_index=case.ignore_index,
-        temperature=case.temperature, eps=case.eps)
+        temperature=case.temperature, eps=case.eps,
+        Xt_rows=None if inp["X_teacher"] is None else H.to_np(inp["X_teacher"][rows]),
+        W_teacher=H.to_np(inp["W_teacher"]), b_teacher=H.to_np(inp["b_teacher"]))
     print(f"[cfg{cfg}] oracle rows done", flush=True)
 
     per = out["per_row"].cpu().double().numpy()

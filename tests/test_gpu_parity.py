@@ -8,6 +8,8 @@ rows are not 16-byte multiples), and BT = 300 / 520 leave a partial last
 token chunk.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -43,6 +45,19 @@ SMALL = {
     "ce-fp32-sum-tau": workloads.small_case(
         BT=90, H=48, V=301, dtype="fp32", head="ce", compute_dW=True, reduction="sum",
         temperature=0.5, x_std=1.0, w_std=0.1, seed=18),
+    # Jensen-Shannon head: the teacher has its own projection of another
+    # hidden size (and a bias), the student a ragged vocabulary
+    "jsd-bf16-ragged-trainable-teacher-bias": workloads.small_case(
+        BT=300, H=264, V=1000, dtype="bf16", head="jsd", has_bias=True, compute_dW=True,
+        compute_db=True, H_teacher=136, teacher_has_bias=True, teacher_w_std=0.05,
+        temperature=2.0, ignore_frac=0.1, reduction="batchmean", w_std=0.05, seed=19),
+    "jsd-bf16-mean-odd-vocab": workloads.small_case(
+        BT=257, H=64, V=777, dtype="bf16", head="jsd", H_teacher=264, reduction="mean",
+        with_labels=False, w_std=0.1, teacher_w_std=0.1, seed=20),
+    "jsd-fp32-sum-tau": workloads.small_case(
+        BT=90, H=48, V=301, dtype="fp32", head="jsd", compute_dW=True, H_teacher=40,
+        reduction="sum", temperature=0.5, ignore_frac=0.2, x_std=1.0, w_std=0.1,
+        teacher_w_std=0.1, seed=21),
     "kl-fp32-sum-ignored": workloads.small_case(
         BT=100, H=40, V=515, dtype="fp32", head="kl", reduction="sum", ignore_frac=0.2,
         compute_dW=True, x_std=1.0, w_std=0.1, temperature=0.75, seed=16),
@@ -220,3 +235,34 @@ def test_ce_per_token_weights():
     inp = H.make(case)
     inp["weights"] = torch.rand(case.BT, generator=torch.Generator().manual_seed(7))
     H.compare_full(H.run_gpu(inp, case), H.run_oracle(inp, case), case)
+
+
+# --------------------------------------------------------------------------
+# Jensen-Shannon head
+# --------------------------------------------------------------------------
+
+def test_jsd_teacher_equal_to_student_gives_zero():
+    # the same projection on both sides: both logits GEMMs produce identical
+    # rows, every log-ratio is exactly 0, so the loss and every gradient are 0
+    case = workloads.small_case(BT=300, H=136, V=1000, dtype="bf16", head="jsd",
+                                has_bias=True, compute_dW=True, compute_db=True,
+                                H_teacher=136, teacher_has_bias=True, temperature=2.0,
+                                w_std=0.05, seed=33)
+    inp = H.make(case)
+    inp["X_teacher"], inp["W_teacher"], inp["b_teacher"] = inp["X"], inp["W"], inp["b"]
+    out = H.run_gpu(inp, case)
+    assert float(out["loss"]) == 0.0
+    for k in ("dX", "dW", "db", "per_row"):
+        assert torch.count_nonzero(out[k]).item() == 0, k
+
+
+def test_jsd_rows_within_bounds_and_dx_independent_of_flags():
+    case = workloads.small_case(BT=520, H=136, V=4099, dtype="bf16", head="jsd",
+                                H_teacher=264, compute_dW=True, ignore_frac=0.05,
+                                w_std=0.2, teacher_w_std=0.2, seed=34)
+    inp = H.make(case)
+    a = H.run_gpu(inp, case)
+    per = a["per_row"].cpu()
+    assert bool((per >= 0).all()) and bool((per <= math.log(2) * (1 + 1e-5)).all())
+    b = H.run_gpu(inp, case.replace(compute_dW=False))
+    assert torch.equal(a["dX"], b["dX"]) and torch.equal(a["loss"], b["loss"])

@@ -15,7 +15,7 @@ from tests import test_oracle_pins as P
 
 _orig = {name: getattr(O, name) for name in
          ("logits", "kl_rows", "selective_rows", "dlogits", "reduction_scale",
-          "valid_rows", "log_softmax")}
+          "valid_rows", "log_softmax", "jsd_rows", "teacher_probs")}
 
 
 def _kl_without_entropy(logP, target, valid, eps):
@@ -84,6 +84,30 @@ def _log_softmax_unshifted_lse(S):
     return logP + 1e-3, lse
 
 
+def _jsd_without_half(logP, teacher, valid):
+    return 2.0 * _orig["jsd_rows"](logP, teacher, valid)
+
+
+def _jsd_as_kl(logP, teacher, valid):
+    # KL(teacher || model) in place of the divergence to the mixture
+    return _orig["kl_rows"](logP, teacher, valid, 1e-300)
+
+
+def _dlogits_jsd_no_mean_term(head, logP, target, labels, w, valid, g, temperature):
+    if head != "jsd":
+        return _orig["dlogits"](head, logP, target, labels, w, valid, g, temperature)
+    P = np.exp(logP)
+    M = 0.5 * (np.asarray(target) + P)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        G = np.where(P > 0, 0.5 * np.log(P / M), 0.0)
+    dS = g * P * G * valid[:, None]
+    return dS / temperature
+
+
+def _teacher_untempered(X_teacher, W_teacher, b_teacher, temperature):
+    return _orig["teacher_probs"](X_teacher, W_teacher, b_teacher, 1.0)
+
+
 def _valid_all_rows(labels, ignore_index, BT):
     return np.ones(BT, dtype=bool)
 
@@ -103,6 +127,10 @@ MUTATIONS = {
     "tau multiplies": ("logits", _logits_tau_multiplies),
     "log-softmax off by a constant": ("log_softmax", _log_softmax_unshifted_lse),
     "ignore mask ignored": ("valid_rows", _valid_all_rows),
+    "JSD drops the one-half": ("jsd_rows", _jsd_without_half),
+    "JSD replaced by KL to the teacher": ("jsd_rows", _jsd_as_kl),
+    "JSD gradient misses the mean term": ("dlogits", _dlogits_jsd_no_mean_term),
+    "teacher logits not tempered": ("teacher_probs", _teacher_untempered),
 }
 
 

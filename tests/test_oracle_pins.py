@@ -258,7 +258,7 @@ def _central_fd(f, args, i, h=1e-6):
 
 
 FD_CASES = []
-for head in ("kl", "selective", "ce"):
+for head in ("kl", "selective", "ce", "jsd"):
     for reduction in ("batchmean", "mean", "sum"):
         for tau in (0.5, 1.0, 2.0):
             FD_CASES.append((head, reduction, tau))
@@ -274,6 +274,8 @@ def test_gradients_central_differences(head, reduction, tau):
     if head == "kl":
         q = _softmax(_rand(BT, V)) * 1.3  # unnormalised: exercises Q_r
         kw["target"] = q
+    elif head == "jsd":
+        kw.update(X_teacher=_rand(BT, 6), W_teacher=_rand(V, 6), b_teacher=_rand(V))
     else:
         kw["weights"] = _rand(BT)
     out = O.fwd_bwd(X, W, b, **kw)
@@ -284,7 +286,7 @@ def test_gradients_central_differences(head, reduction, tau):
                                    err_msg=name)
 
 
-@pytest.mark.parametrize("head", ["kl", "selective", "ce"])
+@pytest.mark.parametrize("head", ["kl", "selective", "ce", "jsd"])
 def test_gradients_match_torch_autograd(head):
     BT, H, V, tau = 33, 24, 57, 2.0
     X, W, b = _rand(BT, H), _rand(V, H, std=0.3), _rand(V)
@@ -304,10 +306,20 @@ def test_gradients_match_torch_autograd(head):
                              ignore_index=-100, reduction="none")
         loss_t = -(torch.tensor(w) * ce).sum() / keep.sum()
         kw = dict(weights=w, reduction="mean")
-    else:
+    elif head == "ce":
         loss_t = F.cross_entropy(F.linear(Xt, Wt, bt) / tau, torch.tensor(labels),
                                  ignore_index=-100, reduction="mean")
         kw = dict(reduction="mean")
+    else:
+        # the Jensen-Shannon divergence written out in torch, differentiated
+        # through the mixture M by autograd (teacher: no gradient)
+        Xte, Wte, bte = _rand(BT, 40), _rand(V, 40, std=0.3), _rand(V)
+        logPt = torch.log_softmax(F.linear(*(torch.tensor(a) for a in (Xte, Wte, bte))) / tau, 1)
+        Pt, Q = logPt.exp(), logP.exp()
+        logM = torch.log(0.5 * (Pt + Q))
+        js = 0.5 * (Pt * (logPt - logM)).sum(1) + 0.5 * (Q * (logP - logM)).sum(1)
+        loss_t = js[torch.tensor(keep)].sum() / keep.sum()
+        kw = dict(reduction="batchmean", X_teacher=Xte, W_teacher=Wte, b_teacher=bte)
     loss_t.backward()
     out = O.fwd_bwd(X, W, b, head=head, labels=labels, temperature=tau, **kw)
     assert out["loss"] == pytest.approx(float(loss_t), rel=1e-12)
@@ -316,17 +328,19 @@ def test_gradients_match_torch_autograd(head):
     np.testing.assert_allclose(out["db"], bt.grad.numpy(), rtol=1e-10, atol=1e-14)
 
 
-@pytest.mark.parametrize("head", ["kl", "selective"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
 def test_dlogit_rows_sum_to_zero(head):
     BT, V = 20, 300
     logP, _ = O.log_softmax(_rand(BT, V, std=3.0))
     labels = rng.integers(0, V, size=BT)
     q = _softmax(_rand(BT, V)) * 0.7  # sum_v (Q p - q) = 0 for any scale
+    if head == "jsd":
+        q = _softmax(_rand(BT, V, std=3.0))  # the teacher distribution
     dZ = O.dlogits(head, logP, q, labels, _rand(BT), np.ones(BT, bool), 0.3, 2.0)
     np.testing.assert_allclose(dZ.sum(axis=1), 0.0, atol=1e-15)
 
 
-@pytest.mark.parametrize("head", ["kl", "selective"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
 def test_temperature_power_of_two_identity(head):
     # S = (X W^T + b)/tau equals X (W/tau)^T + b/tau exactly for tau = 2^k, so
     # dX must agree bitwise, and dW(tau) = dW'(tau=1) / tau: pins where 1/tau
@@ -335,13 +349,20 @@ def test_temperature_power_of_two_identity(head):
     X, W, b = _rand(BT, H), _rand(V, H), _rand(V)
     labels = rng.integers(0, V, size=BT)
     kw = dict(head=head, labels=labels)
+    Xte, Wte, bte = _rand(BT, 6), _rand(V, 6), _rand(V)
     if head == "kl":
         kw["target"] = _softmax(_rand(BT, V))
-    else:
+    elif head != "jsd":
         kw["weights"] = _rand(BT)
     for tau in (0.5, 2.0, 4.0):
-        a = O.fwd_bwd(X, W, b, temperature=tau, **kw)
-        c = O.fwd_bwd(X, W / tau, b / tau, temperature=1.0, **kw)
+        if head == "jsd":  # the temperature divides the teacher's logits too
+            kw.update(X_teacher=Xte, W_teacher=Wte, b_teacher=bte)
+            a = O.fwd_bwd(X, W, b, temperature=tau, **kw)
+            kw.update(W_teacher=Wte / tau, b_teacher=bte / tau)
+            c = O.fwd_bwd(X, W / tau, b / tau, temperature=1.0, **kw)
+        else:
+            a = O.fwd_bwd(X, W, b, temperature=tau, **kw)
+            c = O.fwd_bwd(X, W / tau, b / tau, temperature=1.0, **kw)
         assert a["loss"] == c["loss"]
         np.testing.assert_array_equal(a["dX"], c["dX"])
         np.testing.assert_array_equal(a["dW"], c["dW"] / tau)
@@ -357,7 +378,7 @@ def test_flags_do_not_change_dx():
     assert a["loss"] == c["loss"]
 
 
-@pytest.mark.parametrize("head", ["kl", "selective"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
 def test_sampled_rows_agree_with_full(head):
     BT, H, V = 16, 8, 29
     X, W, b = _rand(BT, H), _rand(V, H), _rand(V)
@@ -365,16 +386,22 @@ def test_sampled_rows_agree_with_full(head):
     labels[[3, 9]] = -100
     kw = dict(head=head, reduction="mean", temperature=2.0)
     q = w = None
+    tk = tsub = {}
     if head == "kl":
         q = _softmax(_rand(BT, V))
+    elif head == "jsd":
+        Xte, Wte, bte = _rand(BT, 5), _rand(V, 5), _rand(V)
+        tk = dict(X_teacher=Xte, W_teacher=Wte, b_teacher=bte)
     else:
         w = _rand(BT)
-    full = O.fwd_bwd(X, W, b, labels=labels, target=q, weights=w, **kw)
+    full = O.fwd_bwd(X, W, b, labels=labels, target=q, weights=w, **kw, **tk)
     rows = np.array([0, 3, 5, 15])
+    if head == "jsd":
+        tsub = dict(Xt_rows=Xte[rows], W_teacher=Wte, b_teacher=bte)
     sub = O.sampled_rows(X[rows], W, b, n_valid=full["n_valid"],
                          labels_rows=labels[rows],
                          target_rows=None if q is None else q[rows],
-                         weights_rows=None if w is None else w[rows], **kw)
+                         weights_rows=None if w is None else w[rows], **kw, **tsub)
     np.testing.assert_array_equal(sub["per_row"], full["per_row"][rows])
     np.testing.assert_allclose(sub["dX"], full["dX"][rows], rtol=1e-14, atol=1e-17)
 
@@ -418,3 +445,48 @@ def test_ce_equals_kl_with_one_hot_target():
         assert a["loss"] == pytest.approx(c["loss"], rel=1e-13)
         for k in ("dX", "dW", "db"):
             np.testing.assert_allclose(a[k], c[k], rtol=1e-12, atol=1e-15, err_msg=k)
+
+
+# --------------------------------------------------------------------------
+# Jensen-Shannon head (teacher with its own projection)
+# --------------------------------------------------------------------------
+
+def test_jsd_zero_when_teacher_is_the_student():
+    # the same projection on both sides: P = Pt, so JS = 0 and every
+    # student gradient vanishes
+    X, W, b = _rand(11, 6), _rand(17, 6), _rand(17)
+    out = O.fwd_bwd(X, W, b, head="jsd", X_teacher=X, W_teacher=W, b_teacher=b,
+                    temperature=0.5, reduction="sum")
+    assert abs(out["loss"]) <= 1e-15
+    for k in ("dX", "dW", "db"):
+        assert np.abs(out[k]).max() <= 1e-15, k
+
+
+def test_jsd_matches_scipy_jensenshannon():
+    # scipy's jensenshannon is the square root of the divergence (natural log)
+    from scipy.spatial.distance import jensenshannon
+    logP, _ = O.log_softmax(_rand(8, 23, std=2.0))
+    Pt = _softmax(_rand(8, 23, std=2.0))
+    ours = O.jsd_rows(logP, Pt, np.ones(8, bool))
+    ref = np.array([jensenshannon(Pt[r], np.exp(logP[r])) ** 2 for r in range(8)])
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_jsd_bounds_and_symmetry():
+    logP, _ = O.log_softmax(_rand(30, 40, std=4.0))
+    logQ, _ = O.log_softmax(_rand(30, 40, std=4.0))
+    a = O.jsd_rows(logP, np.exp(logQ), np.ones(30, bool))
+    c = O.jsd_rows(logQ, np.exp(logP), np.ones(30, bool))
+    np.testing.assert_allclose(a, c, rtol=1e-13)
+    assert (a >= 0).all() and (a <= math.log(2) + 1e-15).all()
+
+
+def test_jsd_disjoint_supports_is_log2():
+    # no common support: M = P/2 on P's support and Q/2 on Q's, so each half
+    # contributes log 2 / 2
+    P = np.array([[0.5, 0.5, 0.0, 0.0], [0.0, 0.0, 0.0, 1.0]])
+    Q = np.array([[0.0, 0.0, 0.3, 0.7], [0.2, 0.3, 0.5, 0.0]])
+    with np.errstate(divide="ignore"):
+        logQ = np.log(Q)
+    L = O.jsd_rows(logQ, P, np.ones(2, bool))
+    np.testing.assert_allclose(L, math.log(2), rtol=1e-15)

@@ -29,6 +29,7 @@ import torch
 HEAD_KL = "kl"
 HEAD_SELECTIVE = "selective"
 HEAD_CE = "ce"
+HEAD_JSD = "jsd"
 
 IGNORE_INDEX = -100
 
@@ -42,7 +43,7 @@ class Case:
     H: int
     V: int
     dtype: str  # "bf16" or "fp32"
-    head: str  # HEAD_KL, HEAD_SELECTIVE or HEAD_CE
+    head: str  # HEAD_KL, HEAD_SELECTIVE, HEAD_CE or HEAD_JSD
     has_bias: bool = False
     compute_dW: bool = False
     compute_db: bool = False
@@ -58,6 +59,10 @@ class Case:
     eps: float = 1e-10
     ignore_index: int = IGNORE_INDEX
     seed: int = 0
+    # JSD head: the teacher's own projection X_t [BT, H_teacher] W_t^T (+ b_t)
+    H_teacher: int = 0
+    teacher_has_bias: bool = False
+    teacher_w_std: float = 0.02
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -88,6 +93,14 @@ CONFIGS = {
 }
 
 
+# The Jensen-Shannon head at the llama-3 head shape: a student and a teacher
+# projection of the same hidden size over V = 128256, frozen student head,
+# 4096 tokens (the distillation batch of the KL workload above).
+JSD_WORKLOAD = Case("jsd-distill-bf16-frozen-V128256", BT=4096, H=4096, V=128256,
+                    dtype="bf16", head=HEAD_JSD, reduction="batchmean", H_teacher=4096,
+                    ignore_frac=0.1, seed=9)
+
+
 def _normal(gen: torch.Generator, shape, std: float) -> torch.Tensor:
     t = torch.empty(shape, dtype=torch.float32)
     t.normal_(0.0, std, generator=gen)
@@ -99,7 +112,9 @@ def make_inputs(case: Case) -> dict:
 
     Returns a dict of CPU tensors: ``X [BT,H]``, ``W [V,H]``, ``b [V]`` or
     None (same dtype as X), ``target [BT,V]`` float32 or None, ``labels
-    [BT]`` int64 or None, ``weights [BT]`` float32 or None, plus ``case``.
+    [BT]`` int64 or None, ``weights [BT]`` float32 or None, the JSD
+    teacher's ``X_teacher [BT,H_t]``, ``W_teacher [V,H_t]``, ``b_teacher
+    [V]`` (else None), plus ``case``.
     """
     gen = torch.Generator("cpu")
     gen.manual_seed(case.seed)
@@ -134,8 +149,16 @@ def make_inputs(case: Case) -> dict:
         if target is not None:
             target[ign] = float("nan")
 
+    # the JSD teacher is drawn last, so the other heads' streams are unchanged
+    X_t = W_t = b_t = None
+    if case.head == HEAD_JSD:
+        X_t = _normal(gen, (BT, case.H_teacher), case.x_std).to(dt)
+        W_t = _normal(gen, (V, case.H_teacher), case.teacher_w_std).to(dt)
+        if case.teacher_has_bias:
+            b_t = _normal(gen, (V,), case.b_std).to(dt)
+
     return dict(X=X, W=W, b=b, target=target, labels=labels, weights=weights,
-                case=case)
+                X_teacher=X_t, W_teacher=W_t, b_teacher=b_t, case=case)
 
 
 def small_case(BT=300, H=264, V=1000, *, dtype="bf16", head=HEAD_KL, seed=100,
