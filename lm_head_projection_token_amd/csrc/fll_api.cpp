@@ -86,9 +86,15 @@ void layout(fll_plan_t *pl, int64_t C) {
   pl->chunk_rows = C;
   pl->n_chunks = p.BT > 0 ? cdiv(p.BT, C) : 0;
   pl->s_pitch = rup(p.V, 64);
-  // The dX split depends on V only, so every row of dX is summed in the same
-  // order whatever the chunk size and whatever the dW/db flags.
-  int64_t splits = std::min<int64_t>(4, std::max<int64_t>(1, cdiv(p.V, 16384)));
+  // The dX GEMM has only C/tile x H/tile output tiles, so its vocabulary
+  // (K) range is split until about 512 workgroups fill the 256 CUs, each
+  // split keeping at least 2048 vocabulary entries. The split depends on the
+  // chunk size but never on the dW/db flags, so dX is bit-identical with and
+  // without them.
+  const int64_t tile = p.dtype == FLL_BF16 ? 256 : 64;
+  const int64_t out_tiles = cdiv(C, tile) * cdiv(p.H, tile);
+  const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(16, p.V / 2048));
+  int64_t splits = std::min(max_splits, std::max<int64_t>(1, cdiv(512, out_tiles)));
   pl->dx_split_len = rup(cdiv(p.V, splits), 64);
   pl->dx_splits = cdiv(p.V, pl->dx_split_len);
   // per-row (max, sum exp) of every 128-column block, from the bf16 logits GEMM
@@ -100,8 +106,15 @@ void layout(fll_plan_t *pl, int64_t C) {
   off = align256(off + size_t(std::max<int64_t>(p.BT, 1)) * 4);
   pl->off_stats = off;
   off = align256(off + size_t(C) * size_t(pl->stat_tiles) * 8);
+  // fp32 partial sums: of the dX splits, and (after dX is reduced) of the
+  // db column sums over kDbSplits row ranges; sized for both whatever the
+  // flags, so C does not depend on them
   pl->off_dx_partial = off;
-  if (pl->dx_splits > 1) off = align256(off + size_t(pl->dx_splits) * C * p.H * 4);
+  {
+    const size_t dx_part = pl->dx_splits > 1 ? size_t(pl->dx_splits) * C * p.H * 4 : 0;
+    const size_t db_part = size_t(fll::kDbSplits) * size_t(p.V) * 4;
+    off = align256(off + std::max(dx_part, db_part));
+  }
   pl->off_scalars = off;
   off = align256(off + sizeof(fll::DevScalars));
   // JSD: the teacher's logits of the chunk and their row statistics
@@ -413,7 +426,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     }
     if (p.compute_db) {
       Probe pr(FLL_K_DB, s);
-      fll::launch_colsum(S, bf16 ? 1 : 0, ldz, rows, p.V, a.db, c > 0, s);
+      fll::launch_colsum(S, bf16 ? 1 : 0, ldz, rows, p.V, partial, a.db, c > 0, s);
       if ((st = hip_check("db column sums"))) return st;
     }
   }

@@ -88,9 +88,11 @@ struct RowArgs {
 };
 void launch_row(const RowArgs &a, hipStream_t st);
 
-// db[v] (+)= sum over rows of dZ[r, v] for v < V.
+// db[v] (+)= sum over rows of dZ[r, v] for v < V: kDbSplits row ranges are
+// summed into P [kDbSplits x V] fp32, then added in a fixed order.
+constexpr int kDbSplits = 16;
 void launch_colsum(const void *dZ, int dz_bf16, int64_t ldz, int64_t rows,
-                   int64_t V, float *db, int accumulate, hipStream_t st);
+                   int64_t V, float *P, float *db, int accumulate, hipStream_t st);
 
 // dX[m, n] = sum_s P[s][m, n] in order s = 0, 1, ...; dX in bf16 or fp32.
 void launch_dx_reduce(const float *P, int64_t splits, int64_t M, int64_t N,

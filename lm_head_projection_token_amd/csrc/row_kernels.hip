@@ -540,43 +540,76 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float *rowval,
   if (threadIdx.x == 0) *loss = float(double(sc->g) * part[0]);
 }
 
-// db column sums: each x-thread owns two adjacent columns, the y-threads split
-// the rows, and the y-partials are added in a fixed order.
-constexpr int kColX = 64, kColY = 4;
+
+// db column sums. Stage 1: block (x, y) sums rows [y R / kDbSplits,
+// (y + 1) R / kDbSplits) of columns 256 x .. 256 x + 255 — each thread four
+// adjacent columns read with one 8-byte (bf16) or 16-byte (fp32) load per
+// row, the four row groups of the block added in a fixed order — into
+// P[y][v]. Stage 2 adds the kDbSplits partials of each column in order, so
+// the result does not depend on scheduling.
+constexpr int kColX = 64, kColY = 4, kColW = 4;
 template <bool BF16>
 __global__ __launch_bounds__(kColX *kColY) void colsum_kernel(const void *dZ, int64_t ldz,
                                                               int64_t rows, int64_t V,
-                                                              float *db, int accumulate) {
-  __shared__ float part[kColY][kColX][2];
+                                                              float *P) {
+  __shared__ float part[kColY][kColX][kColW];
   const int tx = threadIdx.x, ty = threadIdx.y;
-  const int64_t v = (int64_t(blockIdx.x) * kColX + tx) * 2;
-  float s0 = 0.f, s1 = 0.f;
+  const int64_t v = (int64_t(blockIdx.x) * kColX + tx) * kColW;
+  const int64_t r0 = rows * blockIdx.y / kDbSplits, r1 = rows * (blockIdx.y + 1) / kDbSplits;
+  float s[kColW] = {0.f, 0.f, 0.f, 0.f};
   if (v < V) {
-    const bool two = v + 1 < V;
-    for (int64_t r = ty; r < rows; r += kColY) {
+    const bool whole = v + kColW <= V;
+#pragma unroll 4
+    for (int64_t r = r0 + ty; r < r1; r += kColY) {
       if (BF16) {
-        const unsigned short *row = static_cast<const unsigned short *>(dZ) + r * ldz;
-        s0 += __uint_as_float(unsigned(row[v]) << 16);
-        if (two) s1 += __uint_as_float(unsigned(row[v + 1]) << 16);
+        const unsigned short *row = static_cast<const unsigned short *>(dZ) + r * ldz + v;
+        if (whole) {
+          const uint2 u = *reinterpret_cast<const uint2 *>(row);
+          s[0] += __uint_as_float(u.x << 16);
+          s[1] += __uint_as_float(u.x & 0xffff0000u);
+          s[2] += __uint_as_float(u.y << 16);
+          s[3] += __uint_as_float(u.y & 0xffff0000u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kColW; ++e)
+            if (v + e < V) s[e] += __uint_as_float(unsigned(row[e]) << 16);
+        }
       } else {
-        const float *row = static_cast<const float *>(dZ) + r * ldz;
-        s0 += row[v];
-        if (two) s1 += row[v + 1];
+        const float *row = static_cast<const float *>(dZ) + r * ldz + v;
+        if (whole) {
+          const float4 u = *reinterpret_cast<const float4 *>(row);
+          s[0] += u.x;
+          s[1] += u.y;
+          s[2] += u.z;
+          s[3] += u.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < kColW; ++e)
+            if (v + e < V) s[e] += row[e];
+        }
       }
     }
   }
-  part[ty][tx][0] = s0;
-  part[ty][tx][1] = s1;
+#pragma unroll
+  for (int e = 0; e < kColW; ++e) part[ty][tx][e] = s[e];
   __syncthreads();
   if (ty == 0 && v < V) {
-    float t0 = 0.f, t1 = 0.f;
-    for (int y = 0; y < kColY; ++y) {
-      t0 += part[y][tx][0];
-      t1 += part[y][tx][1];
+    float* out = P + int64_t(blockIdx.y) * V;
+#pragma unroll
+    for (int e = 0; e < kColW; ++e) {
+      float t = 0.f;
+      for (int y = 0; y < kColY; ++y) t += part[y][tx][e];
+      if (v + e < V) out[v + e] = t;
     }
-    db[v] = accumulate ? db[v] + t0 : t0;
-    if (v + 1 < V) db[v + 1] = accumulate ? db[v + 1] + t1 : t1;
   }
+}
+
+__global__ void colsum_reduce_kernel(const float *P, int64_t V, float *db, int accumulate) {
+  const int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v >= V) return;
+  float t = 0.f;
+  for (int y = 0; y < kDbSplits; ++y) t += P[int64_t(y) * V + v];
+  db[v] = accumulate ? db[v] + t : t;
 }
 
 __global__ void dx_reduce_kernel(const float *P, int64_t splits, int64_t M, int64_t N,
@@ -627,14 +660,16 @@ void launch_row(const RowArgs &a, hipStream_t st) {
 }
 
 void launch_colsum(const void *dZ, int dz_bf16, int64_t ldz, int64_t rows, int64_t V,
-                   float *db, int accumulate, hipStream_t st) {
-  const int64_t blocks = (V + 2 * kColX - 1) / (2 * kColX);
+                   float *P, float *db, int accumulate, hipStream_t st) {
+  const int64_t blocks = (V + kColX * kColW - 1) / (kColX * kColW);
   if (dz_bf16)
-    hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks), dim3(kColX, kColY), 0, st, dZ,
-                       ldz, rows, V, db, accumulate);
+    hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks, kDbSplits), dim3(kColX, kColY), 0,
+                       st, dZ, ldz, rows, V, P);
   else
-    hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks), dim3(kColX, kColY), 0, st, dZ,
-                       ldz, rows, V, db, accumulate);
+    hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks, kDbSplits), dim3(kColX, kColY), 0,
+                       st, dZ, ldz, rows, V, P);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((V + 255) / 256), dim3(256), 0, st, P, V, db,
+                     accumulate);
 }
 
 void launch_dx_reduce(const float *P, int64_t splits, int64_t M, int64_t N, void *dX,

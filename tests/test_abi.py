@@ -101,14 +101,20 @@ def test_plan_does_not_depend_on_gradient_flags():
         assert getattr(a, f) == getattr(b, f), f
 
 
-def test_plan_dx_split_depends_on_vocab_only():
-    a = fll.fll_plan(_prob(BT=8192))
-    b = fll.fll_plan(_prob(BT=300))
-    c = fll.fll_plan(_prob(BT=8192), 0, 100)
-    assert (a.dx_splits, a.dx_split_len) == (b.dx_splits, b.dx_split_len) == \
-        (c.dx_splits, c.dx_split_len)
-    assert a.dx_splits * a.dx_split_len >= 128256
-    assert (a.dx_splits - 1) * a.dx_split_len < 128256
+def test_plan_dx_split_fills_the_device():
+    # the vocabulary split of the dX GEMM targets ~512 workgroups of 256 x 256
+    # output tiles, keeps >= 2048 vocabulary entries per split, covers V
+    # exactly once, and does not depend on the gradient flags
+    for BT, V, want in ((8192, 128256, 2), (1024, 32000, 15), (300, 1000, 1),
+                        (600, 128256, 16)):
+        for flags in (dict(), dict(compute_dW=True, has_bias=True, compute_db=True)):
+            pl = fll.fll_plan(_prob(BT=BT, V=V, **flags))
+            tiles = -(-pl.chunk_rows // 256) * (4096 // 256)
+            assert pl.dx_splits == want, (BT, V, pl.dx_splits)
+            assert pl.dx_splits * pl.dx_split_len >= V
+            assert (pl.dx_splits - 1) * pl.dx_split_len < V
+            assert pl.dx_splits == 1 or V / pl.dx_splits >= 2048 - 64
+            assert pl.dx_splits * tiles >= 512 or pl.dx_splits == max(1, min(16, V // 2048))
 
 
 def test_plan_budget_shrinks_chunks_then_fails():

@@ -188,6 +188,8 @@ def test_frozen_head_leaves_dw_untouched():
 
 
 def test_chunk_size_does_not_change_dx():
+    # V < 2048: the dX GEMM never splits the vocabulary, so every dX row is
+    # summed in the same order whatever the chunk size
     inp = H.make(BITCASE)
     base = H.run_gpu(inp, BITCASE)
     assert base["plan"].n_chunks >= 2
@@ -201,6 +203,28 @@ def test_chunk_size_does_not_change_dx():
                                    atol=1e-6 * float(base["dW"].abs().max()))
         torch.testing.assert_close(other["db"], base["db"], rtol=1e-5,
                                    atol=1e-6 * float(base["db"].abs().max()))
+
+
+def test_chunk_size_changes_dx_only_by_reassociation():
+    # the vocabulary split of dX follows the chunk size (about 512 workgroups:
+    # 16 splits at C = 512, 11 at C = 768, 8 at C = 1024 here), so dX rows are
+    # fp32 sums in another order: equal to a bf16 rounding step; the per-row
+    # loss terms do not depend on it
+    case = workloads.small_case(BT=1024, H=4096, V=32768, dtype="bf16", head="selective",
+                                compute_dW=True, seed=35)
+    inp = H.make(case)
+    base = H.run_gpu(inp, case)
+    splits = {base["plan"].dx_splits}
+    for C in (768, 1024):
+        other = H.run_gpu(inp, case, chunk_rows=C)
+        splits.add(other["plan"].dx_splits)
+        assert torch.equal(base["per_row"], other["per_row"]), C
+        assert torch.equal(base["loss"], other["loss"]), C
+        torch.testing.assert_close(other["dX"].float(), base["dX"].float(), rtol=2 ** -7,
+                                   atol=1e-3 * float(base["dX"].float().abs().max()))
+        torch.testing.assert_close(other["dW"], base["dW"], rtol=1e-5,
+                                   atol=1e-6 * float(base["dW"].abs().max()))
+    assert len(splits) > 1, splits
 
 
 def test_repeated_calls_are_bitwise_equal():
