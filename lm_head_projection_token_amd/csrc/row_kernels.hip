@@ -80,6 +80,23 @@ __device__ __forceinline__ Load4 load_group(const float *row, int64_t g, int64_t
   return r;
 }
 
+// The same for the last read of a row: a non-temporal load, so the streamed
+// row does not displace reused lines in the caches.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Load4 load_group_last(const float *row, int64_t g, int64_t V,
+                                                 bool vec_ok) {
+  Load4 r;
+  const int64_t e = 4 * g;
+  if (vec_ok && e + 4 <= V) {
+    const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(row + e));
+    r.v[0] = x.x; r.v[1] = x.y; r.v[2] = x.z; r.v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = (e + i < V) ? row[e + i] : 0.0f;
+  }
+  return r;
+}
+
 // Block-wide reduction helpers: wave shuffles, then the four waves' partials
 // combined in a fixed order by thread 0 through LDS.
 __device__ __forceinline__ float block_sum(float v, float (*red)[8], int slot, int lane,
@@ -251,8 +268,8 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t g = base + u * kRowThreads + tid;
       if (g < ngroups) {
-        xs[u] = load_group(Srow, g, V, true);
-        if (HEAD == HEAD_KL) qs[u] = load_group(q, g, V, q_vec);
+        xs[u] = load_group_last(Srow, g, V, true);
+        if (HEAD == HEAD_KL) qs[u] = load_group_last(q, g, V, q_vec);
       }
     }
     __syncthreads();
@@ -452,8 +469,8 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t g = base + u * kRowThreads + tid;
       if (g < ngroups) {
-        xs[u] = load_group(Srow, g, V, true);
-        ys[u] = load_group(Trow, g, V, true);
+        xs[u] = load_group_last(Srow, g, V, true);
+        ys[u] = load_group_last(Trow, g, V, true);
       }
     }
     __syncthreads();

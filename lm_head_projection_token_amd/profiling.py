@@ -89,7 +89,8 @@ def copy_factor(d: str, counter: str, copy_bytes: int) -> float:
     return copy_bytes / counted
 
 
-def kernels_summary(stats_csv: str, workload: str, command: str, out: str) -> None:
+def kernels_summary(stats_csv: str, workload: str, command: str, out: str,
+                    note: str = "") -> None:
     with open(stats_csv) as fh:
         rows = list(csv.DictReader(fh))
     lines = [f"# Kernel trace: {workload}", "",
@@ -102,6 +103,8 @@ def kernels_summary(stats_csv: str, workload: str, command: str, out: str) -> No
             continue
         lines.append(f"| {kind} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
+    if note:
+        lines += ["", note]
     lines += ["", f"Kernel sources sha256: `{source_hash()}`", ""]
     with open(out, "w") as fh:
         fh.write("\n".join(lines))
@@ -148,6 +151,7 @@ def main():
     k.add_argument("--workload", required=True)
     k.add_argument("--command", required=True)
     k.add_argument("--out", required=True)
+    k.add_argument("--note", default="")
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload",
               "--command", "--out"):
@@ -155,7 +159,7 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     args = ap.parse_args()
     if args.cmd == "kernels":
-        kernels_summary(args.stats, args.workload, args.command, args.out)
+        kernels_summary(args.stats, args.workload, args.command, args.out, args.note)
     else:
         traffic_summary(args.fetch, args.write, args.copy_fetch, args.copy_write,
                         args.copy_bytes, args.workload, args.command, args.out)
