@@ -290,3 +290,57 @@ def test_jsd_rows_within_bounds_and_dx_independent_of_flags():
     assert bool((per >= 0).all()) and bool((per <= math.log(2) * (1 + 1e-5)).all())
     b = H.run_gpu(inp, case.replace(compute_dW=False))
     assert torch.equal(a["dX"], b["dX"]) and torch.equal(a["loss"], b["loss"])
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture
+# --------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager():
+    # fll_fwd_bwd only launches kernels (zero fills are kernels too), so it
+    # can be captured into a HIP graph; every replay, with eager work and
+    # synchronisation in between, must reproduce the eager result bitwise
+    import lm_head_projection_token_amd as fll
+
+    case = workloads.small_case(BT=520, H=136, V=777, dtype="bf16", head="selective",
+                                has_bias=True, compute_dW=True, compute_db=True,
+                                reduction="mean", ignore_frac=0.05, w_std=0.05, seed=36)
+    inp = H.make(case)
+    dev = "cuda:0"
+    X, W, b = (inp[k].to(dev) for k in ("X", "W", "b"))
+    labels, weights = inp["labels"].to(dev), inp["weights"].to(dev)
+    prob = fll.make_problem(case.BT, case.H, case.V, dtype="bf16", head="selective",
+                            has_bias=True, compute_dW=True, compute_db=True, reduction="mean")
+    plan = fll.fll_plan(prob)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    outs = dict(dX=torch.empty_like(X), dW=torch.empty(case.V, case.H, device=dev),
+                db=torch.empty(case.V, device=dev), loss=torch.empty((), device=dev),
+                per_row=torch.empty(case.BT, device=dev))
+
+    def call(stream=None):
+        fll.fll_fwd_bwd(plan, X=X, W=W, b=b, labels=labels, weights=weights, workspace=ws,
+                        stream=stream, **outs)
+
+    call()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    for v in outs.values():
+        v.fill_(float("nan"))
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream())
+    for rep in range(3):
+        for v in outs.values():
+            v.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v, eager[k]), (rep, k)
