@@ -96,7 +96,7 @@ def test_all_rows_ignored(dtype):
         assert torch.count_nonzero(out[k]).item() == 0, k
 
 
-@pytest.mark.parametrize("head", ["kl", "selective"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
 def test_empty_batch(head):
     import lm_head_projection_token_amd as fll
 
@@ -107,6 +107,9 @@ def test_empty_batch(head):
     kw = dict(labels=torch.empty(0, dtype=torch.int64, device=dev))
     if head == "kl":
         kw["target"] = torch.empty(0, 50, device=dev)
+    if head == "jsd":
+        kw["X_teacher"] = torch.empty(0, 32, dtype=torch.bfloat16, device=dev)
+        kw["W_teacher"] = torch.randn(50, 32, device=dev).to(torch.bfloat16)
     out = fll.fused_lm_head_loss(X, W, b, head=head, compute_dW=True, compute_db=True, **kw)
     torch.cuda.synchronize()
     assert float(out["loss"]) == 0.0
@@ -115,11 +118,12 @@ def test_empty_batch(head):
     assert torch.count_nonzero(out["db"]).item() == 0
 
 
-@pytest.mark.parametrize("head", ["kl", "selective"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
 def test_single_token_vocabulary(head):
     # V = 1: log p = 0 for every row, so the loss and every gradient vanish.
+    extra = dict(H_teacher=24) if head == "jsd" else {}
     case = workloads.small_case(BT=40, H=16, V=1, dtype="bf16", head=head,
-                                compute_dW=True, seed=23)
+                                compute_dW=True, seed=23, **extra)
     inp = H.make(case)
     out = H.run_gpu(inp, case)
     ref = H.run_oracle(inp, case)
