@@ -93,8 +93,23 @@ __device__ __forceinline__ int swz_mn(int k) {
   return (0x6ca0 >> ((k & 3) * 4)) & 15;  // {0, 10, 12, 6}[k & 3]
 }
 
+// Buffer descriptor of `bytes` bytes from `base` (clamped to [0, 2^31 - 1]).
+// The clamp works on the two 32-bit halves: with 64-bit signed compares the
+// compiler emits vector compares writing scalar registers, and the scalar
+// selects waiting on them stall the wavefront inside the MFMA stream.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
-  const int64_t n = bytes <= 0 ? 0 : (bytes > int64_t(kMaxRecords) ? int64_t(kMaxRecords) : bytes);
+  const uint64_t u = uint64_t(bytes);
+  const unsigned hi = unsigned(u >> 32), lo = unsigned(u);
+  unsigned n;
+  asm("s_cmp_eq_u32 %[hi], 0\n\t"              // fits in 32 bits?
+      "s_cselect_b32 %[n], %[lo], %[mx]\n\t"
+      "s_cmp_gt_u32 %[n], %[mx]\n\t"            // above 2^31 - 1?
+      "s_cselect_b32 %[n], %[mx], %[n]\n\t"
+      "s_cmp_lt_i32 %[hi], 0\n\t"               // negative?
+      "s_cselect_b32 %[n], 0, %[n]"
+      : [n] "=&s"(n)
+      : [lo] "s"(lo), [hi] "s"(hi), [mx] "s"(kMaxRecords)
+      : "scc");
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
                                            kRsrcWord3);
 }
