@@ -36,12 +36,14 @@ METRIC = "fwd+bwd tokens/sec at H=4096,V=128256 bf16; % of bf16 MFMA peak"
 COPY_BYTES = 1 << 30
 
 
-def measured_traffic(case, kind):
+def measured_traffic(case, kind, logits_bf16=False):
     """HBM bytes per launch of `kind` from the committed counter summary of
-    this workload, or None if there is none or the kernels changed since."""
+    this workload (and chunk-logits type), or None if there is none or the
+    kernels changed since."""
     from lm_head_projection_token_amd import profiling
 
-    path = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
+    tag = case.name + ("-bf16-logits" if logits_bf16 else "")
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -71,10 +73,13 @@ def kernel_flops(kind, case):
             "teacher": 2.0 * case.BT * case.H_teacher * case.V}.get(kind, 0.0)
 
 
-def row_bytes_per_valid_row(case):
+def row_bytes_per_valid_row(case, logits_bf16=False):
     """Algorithmic HBM bytes of the row kernel per valid row: one read of the
-    logits (and of the target or the teacher's logits) and one write of dZ."""
-    return (10 if case.head in ("kl", "jsd") else 6) * case.V
+    logits (and of the fp32 target or the teacher's logits) and one write of
+    the bf16 dZ; logits are 4 bytes each, or 2 when kept in bf16."""
+    s = 2 if logits_bf16 else 4
+    extra = {"kl": 4, "jsd": s}.get(case.head, 0)
+    return (s + extra + 2) * case.V
 
 
 def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
@@ -134,6 +139,8 @@ def main():
     ap.add_argument("--config", default="3", choices=["2", "3", "4", "5", "jsd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-rows", type=int, default=0)
+    ap.add_argument("--logits-bf16", action="store_true",
+                    help="keep each chunk's logits in bf16 instead of fp32")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -176,7 +183,8 @@ def main():
                             compute_db=case.compute_db, reduction=case.reduction,
                             ignore_index=case.ignore_index, temperature=case.temperature,
                             eps=case.eps, H_teacher=case.H_teacher,
-                            teacher_has_bias=case.teacher_has_bias)
+                            teacher_has_bias=case.teacher_has_bias,
+                            logits_bf16=args.logits_bf16)
     plan = fll.fll_plan(prob, 0, args.chunk_rows)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     dX = torch.empty_like(X)
@@ -226,11 +234,11 @@ def main():
     achieved = per_launch / (kernels[dom]["avg_ms"] / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": measured_traffic(case, dom),
+                "traffic": measured_traffic(case, dom, args.logits_bf16),
                 "flops_per_launch": per_launch}
     row = kernels.get("row")
     if row:
-        bytes_per_row = row_bytes_per_valid_row(case)
+        bytes_per_row = row_bytes_per_valid_row(case, args.logits_bf16)
         n_valid = case.BT if inp["labels"] is None else int(
             (inp["labels"] != case.ignore_index).sum())
         row_bytes = bytes_per_row * n_valid / plan.n_chunks
@@ -244,7 +252,9 @@ def main():
         "config": {"workload": case.name, "BT": case.BT, "H": case.H, "V": case.V,
                    "head": case.head, **({"H_teacher": case.H_teacher} if case.head == "jsd" else {}), "compute_dW": case.compute_dW,
                    "compute_db": case.compute_db, "chunk_rows": plan.chunk_rows,
-                   "n_chunks": plan.n_chunks, "parallelism": "single GPU"},
+                   "n_chunks": plan.n_chunks,
+                   "chunk_logits": "bf16" if args.logits_bf16 else "fp32",
+                   "parallelism": "single GPU"},
         "end_to_end_frac_of_bf16_peak": e2e_frac,
         "wall_s": wall,
         "roofline": roofline,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FLL_VERSION 2
+#define FLL_VERSION 3
 
 /* A hipStream_t, passed opaquely. NULL means the null (default) stream. */
 typedef void *fll_stream;
@@ -113,7 +113,17 @@ typedef struct {
   int64_t H_teacher;    /* JSD: the teacher's hidden size, >= 8 and a multiple
                            of 8; every other head: 0                          */
   int32_t teacher_has_bias; /* JSD: 0/1, b_teacher is given; otherwise 0      */
-  int32_t reserved;     /* 0                                                  */
+  int32_t logits_bf16;  /* bf16 problems, 0/1: keep each chunk's logits (and
+                           the JSD teacher's) in bf16, rounded to nearest even,
+                           instead of fp32. Halves the chunk buffer and the
+                           bytes its logits GEMM writes and its row kernel
+                           reads; the per-row log-sum-exp is still formed from
+                           the fp32 accumulators, so only each p_v and the
+                           label's logit see the rounding. The dlogits then
+                           overwrite the logits element for element. 0 keeps
+                           the fp32 chunk temporaries the method describes
+                           [FusedLinearKLDivLoss page, Details] and is the
+                           default. fp32 problems: 0.                        */
 } fll_problem;
 
 /* The plan: a value type (nothing to free). Its fields after `p` are the
@@ -123,7 +133,8 @@ typedef struct {
   fll_problem p;
   int64_t chunk_rows;     /* C: token rows per chunk                        */
   int64_t n_chunks;       /* ceil(BT / C)                                   */
-  int64_t s_pitch;        /* floats per row of the chunk's logits buffer    */
+  int64_t s_pitch;        /* elements per row of the chunk's logits buffer
+                             (fp32, or bf16 with logits_bf16)               */
   int64_t dx_splits;      /* dX split over the vocabulary (depends on V only)*/
   int64_t dx_split_len;   /* vocabulary columns per dX split                */
   int64_t stat_tiles;     /* per-row statistics tiles (logits GEMM columns) */

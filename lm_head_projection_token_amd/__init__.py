@@ -54,7 +54,7 @@ class FllProblem(ctypes.Structure):
         ("compute_db", ctypes.c_int32), ("reduction", ctypes.c_int32),
         ("ignore_index", ctypes.c_int64), ("temperature", ctypes.c_float),
         ("eps", ctypes.c_float), ("H_teacher", ctypes.c_int64),
-        ("teacher_has_bias", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("teacher_has_bias", ctypes.c_int32), ("logits_bf16", ctypes.c_int32),
     ]
 
 
@@ -155,14 +155,14 @@ def _check(status: int):
 def make_problem(BT, H, V, *, dtype="bf16", head="kl", has_bias=False, compute_dW=False,
                  compute_db=False, reduction="batchmean", ignore_index=-100,
                  temperature=1.0, eps=1e-10, H_teacher=0,
-                 teacher_has_bias=False) -> FllProblem:
+                 teacher_has_bias=False, logits_bf16=False) -> FllProblem:
     return FllProblem(
         BT=BT, H=H, V=V, dtype=DTYPES[dtype] if isinstance(dtype, str) else dtype,
         head=HEADS[head] if isinstance(head, str) else head,
         has_bias=int(has_bias), compute_dW=int(compute_dW), compute_db=int(compute_db),
         reduction=REDUCTIONS[reduction] if isinstance(reduction, str) else reduction,
         ignore_index=ignore_index, temperature=temperature, eps=eps, H_teacher=H_teacher,
-        teacher_has_bias=int(teacher_has_bias), reserved=0)
+        teacher_has_bias=int(teacher_has_bias), logits_bf16=int(logits_bf16))
 
 
 def fll_plan(problem: FllProblem, max_workspace_bytes: int = 0,
@@ -229,10 +229,12 @@ def fll_profile_read(reset: bool = False) -> dict:
 def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=None,
                        reduction="batchmean", ignore_index=-100, temperature=1.0, eps=1e-10,
                        compute_dW=False, compute_db=False, chunk_rows=0, per_row=False,
-                       workspace=None, X_teacher=None, W_teacher=None, b_teacher=None):
+                       workspace=None, X_teacher=None, W_teacher=None, b_teacher=None,
+                       logits_bf16=False):
     """Allocate outputs with torch and run the fused loss. Returns a dict with
     loss (0-dim fp32 tensor), dX, dW, db and (if asked) per_row. The JSD head
-    takes the teacher's X_teacher [BT, H_t], W_teacher [V, H_t] (+ b_teacher)."""
+    takes the teacher's X_teacher [BT, H_t], W_teacher [V, H_t] (+ b_teacher).
+    logits_bf16 keeps the chunk logits in bf16 (bf16 inputs only)."""
     import torch
 
     dev = X.device
@@ -243,7 +245,8 @@ def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=
     prob = make_problem(BT, H, V, dtype=dtype, head=head, has_bias=b is not None,
                         compute_dW=compute_dW, compute_db=compute_db, reduction=reduction,
                         ignore_index=ignore_index, temperature=temperature, eps=eps,
-                        H_teacher=H_t, teacher_has_bias=b_teacher is not None)
+                        H_teacher=H_t, teacher_has_bias=b_teacher is not None,
+                        logits_bf16=logits_bf16)
     plan = fll_plan(prob, 0, chunk_rows)
     if workspace is None or workspace.numel() < plan.workspace_bytes:
         workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)

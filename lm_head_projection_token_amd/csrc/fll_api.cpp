@@ -61,7 +61,10 @@ int check_problem(const fll_problem *p) {
   } else if (p->H_teacher != 0 || p->teacher_has_bias != 0) {
     return fail(FLL_ERR_INVALID_ARG, "H_teacher and teacher_has_bias are for the JSD head");
   }
-  if (p->reserved != 0) return fail(FLL_ERR_INVALID_ARG, "reserved must be 0");
+  if (p->logits_bf16 != 0 && p->logits_bf16 != 1)
+    return fail(FLL_ERR_INVALID_ARG, "flags must be 0 or 1");
+  if (p->logits_bf16 && p->dtype != FLL_BF16)
+    return fail(FLL_ERR_INVALID_ARG, "logits_bf16 is for bf16 problems");
   if (p->BT < 0) return fail(FLL_ERR_INVALID_ARG, "BT < 0");
   if (p->V < 1) return fail(FLL_ERR_INVALID_ARG, "V must be >= 1");
   if (p->H < 8 || p->H % 8 != 0)
@@ -100,8 +103,9 @@ void layout(fll_plan_t *pl, int64_t C) {
   // per-row (max, sum exp) of every 128-column block, from the bf16 logits GEMM
   pl->stat_tiles = p.dtype == FLL_BF16 ? cdiv(p.V, 128) : 0;
   size_t off = 0;
+  const size_t s_elem = p.logits_bf16 ? 2 : 4;  // bytes per chunk logit
   pl->off_logits = off;
-  off = align256(off + size_t(C) * size_t(pl->s_pitch) * 4);
+  off = align256(off + size_t(C) * size_t(pl->s_pitch) * s_elem);
   pl->off_rowval = off;
   off = align256(off + size_t(std::max<int64_t>(p.BT, 1)) * 4);
   pl->off_stats = off;
@@ -121,7 +125,7 @@ void layout(fll_plan_t *pl, int64_t C) {
   pl->off_teacher = off;
   pl->off_teacher_stats = off;
   if (p.head == FLL_HEAD_JSD) {
-    off = align256(off + size_t(C) * size_t(pl->s_pitch) * 4);
+    off = align256(off + size_t(C) * size_t(pl->s_pitch) * s_elem);
     pl->off_teacher_stats = off;
     off = align256(off + size_t(C) * size_t(pl->stat_tiles) * 8);
   }
@@ -350,8 +354,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       Probe pr(FLL_K_TEACHER, s);
       if (bf16)
         fll::launch_logits_bf16(Xtc, p.H_teacher, a.W_teacher, p.H_teacher, a.b_teacher,
-                                inv_tau, T, plan->s_pitch, stats_t, plan->stat_tiles, rows,
-                                p.V, p.H_teacher, s);
+                                inv_tau, T, plan->s_pitch, p.logits_bf16, stats_t,
+                                plan->stat_tiles, rows, p.V, p.H_teacher, s);
       else
         fll::launch_logits_f32(reinterpret_cast<const float *>(Xtc), p.H_teacher,
                                static_cast<const float *>(a.W_teacher), p.H_teacher,
@@ -362,8 +366,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     {
       Probe pr(FLL_K_LOGITS, s);
       if (bf16)
-        fll::launch_logits_bf16(Xc, p.H, a.W, p.H, a.b, inv_tau, S, plan->s_pitch, stats,
-                                plan->stat_tiles, rows, p.V, p.H, s);
+        fll::launch_logits_bf16(Xc, p.H, a.W, p.H, a.b, inv_tau, S, plan->s_pitch,
+                                p.logits_bf16, stats, plan->stat_tiles, rows, p.V, p.H, s);
       else
         fll::launch_logits_f32(reinterpret_cast<const float *>(Xc), p.H,
                                static_cast<const float *>(a.W), p.H,
@@ -380,6 +384,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       ra.V = p.V;
       ra.head = p.head;
       ra.dz_bf16 = bf16 ? 1 : 0;
+      ra.s_bf16 = p.logits_bf16;
       ra.labels = a.labels;
       ra.ignore_index = p.ignore_index;
       ra.target = a.target;
@@ -396,9 +401,10 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       fll::launch_row(ra, s);
     }
     if ((st = hip_check("row kernel"))) return st;
-    // dZ: bf16 packed at the start of each logits row (pitch 2 * s_pitch
-    // elements), or fp32 in place (pitch s_pitch).
-    const int64_t ldz = bf16 ? 2 * plan->s_pitch : plan->s_pitch;
+    // dZ: bf16 packed at the start of each fp32 logits row (pitch
+    // 2 * s_pitch elements), bf16 over bf16 logits (pitch s_pitch), or fp32
+    // in place (pitch s_pitch).
+    const int64_t ldz = bf16 && !p.logits_bf16 ? 2 * plan->s_pitch : plan->s_pitch;
     {
       Probe pr(FLL_K_DX, s);
       if (bf16)

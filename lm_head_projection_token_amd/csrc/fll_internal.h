@@ -17,13 +17,15 @@ struct DevScalars {
 // ---- bf16 MFMA GEMMs (gemm_bf16.hip) --------------------------------------
 
 // S[m, n] = (sum_k X[m, k] W[n, k] + b[n]) * inv_tau for m < M, n < N.
-// X: [M x K] row pitch ldx; W: [N x K] row pitch ldw; S row pitch lds (floats).
+// X: [M x K] row pitch ldx; W: [N x K] row pitch ldw; S row pitch lds
+// elements, fp32, or bf16 (round to nearest even) when s_bf16.
 // If stats != nullptr, also writes for every row m and 128-column block t
-// the block's max and sum of exp(S - max): stats[m * n_stat + t] = (max, sum),
-// n_stat = ceil(N / 128).
+// the block's max and sum of exp(S - max) of the fp32 values:
+// stats[m * n_stat + t] = (max, sum), n_stat = ceil(N / 128).
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
-                        const void *b, float inv_tau, float *S, int64_t lds, float2 *stats,
-                        int64_t n_stat, int64_t M, int64_t N, int64_t K, hipStream_t st);
+                        const void *b, float inv_tau, void *S, int64_t lds, int s_bf16,
+                        float2 *stats, int64_t n_stat, int64_t M, int64_t N, int64_t K,
+                        hipStream_t st);
 
 // dX = dZ W. dZ: bf16 [M x K] row pitch ldz (elements); W: [K x N] pitch ldw.
 // splits == 1: writes bf16 dX [M x N] (pitch ldo). splits > 1: writes fp32
@@ -61,13 +63,16 @@ void launch_prep(const int64_t *labels, int64_t BT, int64_t ignore_index,
 // The fused row kernel over the rows [row0, row0 + rows) of one chunk. With
 // stats it forms log-sum-exp from the logits GEMM's block statistics and
 // streams the logits once; without, it takes a first pass for max / sum exp.
-// S: the chunk's tempered logits (fp32, pitch s_pitch floats). On return the
-// first V entries of each row hold dZ = dS / tau: bf16 packed at the start of
-// the row (bf16 pitch 2 * s_pitch) when dz_bf16, else fp32 in place.
-// rowval[r] receives KL_r or log p(y_r) (0 when ignored).
+// S: the chunk's tempered logits, pitch s_pitch elements, fp32 or (s_bf16)
+// bf16. On return the first V entries of each row hold dZ = dS / tau: over
+// bf16 logits element for element; over fp32 logits bf16 packed at the start
+// of the row (bf16 pitch 2 * s_pitch) when dz_bf16, else fp32 in place.
+// rowval[r] receives KL_r or log p(y_r) (0 when ignored). T (JSD) has S's
+// element type and pitch.
 struct RowArgs {
   float *S;
   int64_t s_pitch;
+  int s_bf16;     // S and T hold bf16 (then dz_bf16 is 1)
   int64_t rows;
   int64_t row0;   // global index of the chunk's first row
   int64_t V;

@@ -258,10 +258,21 @@ struct GemmDesc {
 // Logits epilogue: S = (acc + b[n]) * inv_tau, fp32, plus the row statistics
 // of each 128-column half-tile: max and sum of exp(S - max) over its columns
 // below N, written as stats[m * n_stat + n / 128] (when stats is given).
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// Logits epilogue: S row-major, pitch lds elements, fp32 or (B16) bf16
+// rounded to nearest even. Stores four consecutive columns n .. n + 3 of row
+// m (n is a multiple of 4).
+template <bool B16>
 struct EpiLogits {
   static constexpr bool kRowStats = true;
   static constexpr bool kReadModifyWrite = false;
-  float *S;
+  void *S;
   int64_t lds;
   const unsigned short *bias;
   float inv_tau;
@@ -272,28 +283,31 @@ struct EpiLogits {
   }
   // store4_in: the four columns are inside the matrix
   __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int) const {
-    *reinterpret_cast<f32x4 *>(S + m * lds + n) = v;
+    if constexpr (B16) {
+      uint2 pk;
+      pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
+      pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<unsigned short *>(S) + m * lds + n) = pk;
+    } else {
+      *reinterpret_cast<f32x4 *>(static_cast<float *>(S) + m * lds + n) = v;
+    }
   }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,
                                          int) const {
-    float *p = S + m * lds + n;
     if (n + 4 <= nmax) {
-      *reinterpret_cast<float4 *>(p) = v;
+      store4_in(m, n, f32x4{v.x, v.y, v.z, v.w}, 0);
     } else {
       const float ve[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < nmax) p[e] = ve[e];
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < nmax) {
+          if constexpr (B16) static_cast<unsigned short *>(S)[m * lds + n + e] = f2bf(ve[e]);
+          else static_cast<float *>(S)[m * lds + n + e] = ve[e];
+        }
+      }
     }
   }
 };
-
-__device__ __forceinline__ unsigned short f2bf(float f) {
-  unsigned int u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
 
 // dX epilogue: bf16 store when unsplit, fp32 partial per split otherwise.
 // Stores four consecutive columns n .. n + 3 of row m (n is a multiple of 4).
@@ -742,8 +756,9 @@ void launch(const GemmDesc &d0, const Epi &epi, hipStream_t st) {
 }  // namespace
 
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
-                        const void *b, float inv_tau, float *S, int64_t lds, float2 *stats,
-                        int64_t n_stat, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                        const void *b, float inv_tau, void *S, int64_t lds, int s_bf16,
+                        float2 *stats, int64_t n_stat, int64_t M, int64_t N, int64_t K,
+                        hipStream_t st) {
   GemmDesc d{};
   d.A = static_cast<const unsigned short *>(X);
   d.lda = ldx;
@@ -757,8 +772,11 @@ void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
   d.group = 4;        // measured best for the head shapes: see the tile-order note
   d.n_first = 0;
   d.xcd_remap = 1;
-  EpiLogits e{S, lds, static_cast<const unsigned short *>(b), inv_tau, stats, n_stat};
-  launch<true, true>(d, e, st);
+  const auto *bias = static_cast<const unsigned short *>(b);
+  if (s_bf16)
+    launch<true, true>(d, EpiLogits<true>{S, lds, bias, inv_tau, stats, n_stat}, st);
+  else
+    launch<true, true>(d, EpiLogits<false>{S, lds, bias, inv_tau, stats, n_stat}, st);
 }
 
 void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw, void *dX,

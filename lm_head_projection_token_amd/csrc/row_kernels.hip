@@ -97,6 +97,49 @@ __device__ __forceinline__ Load4 load_group_last(const float *row, int64_t g, in
   return r;
 }
 
+// A row of the chunk's logits: fp32, or (SB) bf16 widened to fp32 on load.
+__device__ __forceinline__ float bf2f(unsigned short h) { return __uint_as_float(unsigned(h) << 16); }
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+template <bool SB>
+struct SRow;
+template <>
+struct SRow<false> {
+  const float *p;
+  __device__ __forceinline__ Load4 load(int64_t g, int64_t V) const {
+    return load_group(p, g, V, true);
+  }
+  __device__ __forceinline__ Load4 load_last(int64_t g, int64_t V) const {
+    return load_group_last(p, g, V, true);
+  }
+  __device__ __forceinline__ float at(int64_t v) const { return p[v]; }
+};
+template <>
+struct SRow<true> {
+  const unsigned short *p;  // rows are 128-byte aligned, so groups are 8-byte aligned
+  template <bool LAST>
+  __device__ __forceinline__ Load4 get(int64_t g, int64_t V) const {
+    Load4 r;
+    const int64_t e = 4 * g;
+    if (e + 4 <= V) {
+      const u32x2_t *q = reinterpret_cast<const u32x2_t *>(p + e);
+      const u32x2_t x = LAST ? __builtin_nontemporal_load(q) : *q;
+      r.v[0] = __uint_as_float(x.x << 16);
+      r.v[1] = __uint_as_float(x.x & 0xffff0000u);
+      r.v[2] = __uint_as_float(x.y << 16);
+      r.v[3] = __uint_as_float(x.y & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.v[i] = (e + i < V) ? bf2f(p[e + i]) : 0.0f;
+    }
+    return r;
+  }
+  __device__ __forceinline__ Load4 load(int64_t g, int64_t V) const { return get<false>(g, V); }
+  __device__ __forceinline__ Load4 load_last(int64_t g, int64_t V) const {
+    return get<true>(g, V);
+  }
+  __device__ __forceinline__ float at(int64_t v) const { return bf2f(p[v]); }
+};
+
 // Block-wide reduction helpers: wave shuffles, then the four waves' partials
 // combined in a fixed order by thread 0 through LDS.
 __device__ __forceinline__ float block_sum(float v, float (*red)[8], int slot, int lane,
@@ -109,7 +152,7 @@ __device__ __forceinline__ float block_sum(float v, float (*red)[8], int slot, i
   return t;
 }
 
-template <int HEAD>
+template <int HEAD, bool SB>
 __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   __shared__ float red[kRowWaves][8];
   __shared__ float bcast[8];
@@ -119,8 +162,10 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   const int64_t lr = blockIdx.x;
   const int64_t gr = a.row0 + lr;
   const int64_t V = a.V;
-  float *Srow = a.S + lr * a.s_pitch;
-  unsigned short *Zb = reinterpret_cast<unsigned short *>(Srow);  // bf16 dZ
+  char *rowp = reinterpret_cast<char *>(a.S) + lr * a.s_pitch * (SB ? 2 : 4);
+  float *Srow = reinterpret_cast<float *>(rowp);                 // fp32 logits / dZ
+  unsigned short *Zb = reinterpret_cast<unsigned short *>(rowp);  // bf16 dZ
+  SRow<SB> sr{reinterpret_cast<decltype(SRow<SB>::p)>(rowp)};
   const int64_t ngroups = (V + 3) / 4;
 
   int64_t y = 0;
@@ -136,13 +181,13 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
       const int64_t e = 4 * g;
       for (int i = 0; i < 4; ++i) {
         if (e + i < V) {
-          if (a.dz_bf16) Zb[e + i] = 0;
+          if (SB || a.dz_bf16) Zb[e + i] = 0;
           else Srow[e + i] = 0.0f;
         }
       }
     }
     if (tid == 0) a.rowval[gr] = bad_label ? NAN : 0.0f;
-    if (a.dz_bf16) zero_pad(Zb, V, tid);
+    if (SB || a.dz_bf16) zero_pad(Zb, V, tid);
     return;
   }
 
@@ -175,7 +220,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     }
   } else {
     for (int64_t g = tid; g < ngroups; g += kRowThreads) {
-      Load4 x = load_group(Srow, g, V, true);
+      Load4 x = sr.load(g, V);
       const int64_t e = 4 * g;
       float mx = -INFINITY;
 #pragma unroll
@@ -203,7 +248,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     }
   }
   float s_label = 0.0f;
-  if (HEAD != HEAD_KL && tid == 0) s_label = Srow[y];  // read before any write
+  if (HEAD != HEAD_KL && tid == 0) s_label = sr.at(y);  // read before any write
 
   // wave reduction, then across waves in a fixed order
   {
@@ -257,9 +302,11 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   }
 
   // ---- dZ = dS / tau, written in place ----
-  // The bf16 dZ of element v goes to bytes [2v, 2v + 2) of the row, i.e. over
-  // float slots that an earlier strip (or this strip, before the barrier)
-  // has already read. Each strip's loads complete before its barrier.
+  // The bf16 dZ of element v goes to bytes [2v, 2v + 2) of the row. Over
+  // fp32 logits those are float slots that an earlier strip (or this strip,
+  // before the barrier) has already read; each strip's loads complete before
+  // its barrier. Over bf16 logits each thread overwrites only the elements
+  // it has just read, so no barrier is needed.
   float bq = 0.0f;  // KL with block statistics: sum q S, accumulated here
   for (int64_t base = 0; base < ngroups; base += kStrip) {
     Load4 xs[kUnroll];
@@ -268,11 +315,11 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t g = base + u * kRowThreads + tid;
       if (g < ngroups) {
-        xs[u] = load_group_last(Srow, g, V, true);
+        xs[u] = sr.load_last(g, V);
         if (HEAD == HEAD_KL) qs[u] = load_group_last(q, g, V, q_vec);
       }
     }
-    __syncthreads();
+    if constexpr (!SB) __syncthreads();
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t g = base + u * kRowThreads + tid;
@@ -289,7 +336,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
           d[i] = coef * (((e + i) == y ? 1.0f : 0.0f) - p);
         }
       }
-      if (a.dz_bf16) {
+      if (SB || a.dz_bf16) {
         if (e + 4 <= V) {
           uint2 pk;
           pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
@@ -314,7 +361,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     if (tid == 0) a.rowval[gr] = bcast[2] - B + Qr * l;
   }
   // Every read of this row finished before the last strip's barrier.
-  if (a.dz_bf16) zero_pad(Zb, V, tid);
+  if (SB || a.dz_bf16) zero_pad(Zb, V, tid);
 }
 
 // Jensen-Shannon head [FusedLinearKLDivLoss page, Summary: the fused JSD
@@ -346,6 +393,7 @@ __device__ __forceinline__ JsdTerms jsd_terms(float s, float t, float lse_s, flo
   return JsdTerms{q, gq, p * gp, q * gq};
 }
 
+template <bool SB>
 __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
   __shared__ float red[kRowWaves][8];
   __shared__ float bcast[8];
@@ -355,9 +403,13 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
   const int64_t lr = blockIdx.x;
   const int64_t gr = a.row0 + lr;
   const int64_t V = a.V;
-  float *Srow = a.S + lr * a.s_pitch;
-  const float *Trow = a.T + lr * a.s_pitch;
-  unsigned short *Zb = reinterpret_cast<unsigned short *>(Srow);  // bf16 dZ
+  const int64_t row_bytes = a.s_pitch * (SB ? 2 : 4);
+  char *rowp = reinterpret_cast<char *>(a.S) + lr * row_bytes;
+  const char *trowp = reinterpret_cast<const char *>(a.T) + lr * row_bytes;
+  float *Srow = reinterpret_cast<float *>(rowp);                 // fp32 logits / dZ
+  unsigned short *Zb = reinterpret_cast<unsigned short *>(rowp);  // bf16 dZ
+  using P = decltype(SRow<SB>::p);
+  SRow<SB> sr{reinterpret_cast<P>(rowp)}, tr{reinterpret_cast<P>(trowp)};
   const int64_t ngroups = (V + 3) / 4;
 
   const bool valid = !a.labels || a.labels[gr] != a.ignore_index;
@@ -366,12 +418,12 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
       const int64_t e = 4 * g;
       for (int i = 0; i < 4; ++i)
         if (e + i < V) {
-          if (a.dz_bf16) Zb[e + i] = 0;
+          if (SB || a.dz_bf16) Zb[e + i] = 0;
           else Srow[e + i] = 0.0f;
         }
     }
     if (tid == 0) a.rowval[gr] = 0.0f;
-    if (a.dz_bf16) zero_pad(Zb, V, tid);
+    if (SB || a.dz_bf16) zero_pad(Zb, V, tid);
     return;
   }
 
@@ -387,7 +439,7 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
     }
   } else {
     for (int64_t g = tid; g < ngroups; g += kRowThreads) {
-      const Load4 x = load_group(Srow, g, V, true), y = load_group(Trow, g, V, true);
+      const Load4 x = sr.load(g, V), y = tr.load(g, V);
       const int64_t e = 4 * g;
       float mx = -INFINITY, my = -INFINITY;
 #pragma unroll
@@ -434,7 +486,7 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
   // ---- pass 1: both halves of the divergence
   float A = 0.0f, B = 0.0f;
   for (int64_t g = tid; g < ngroups; g += kRowThreads) {
-    const Load4 x = load_group(Srow, g, V, true), y = load_group(Trow, g, V, true);
+    const Load4 x = sr.load(g, V), y = tr.load(g, V);
     const int64_t e = 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -460,20 +512,21 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
   const float coef = a.sc->g * a.inv_tau;  // dZ = g (dJS/dS) / tau
   const float half_b = 0.5f * Br;
 
-  // ---- pass 2: dZ in place, strip by strip (every load of a strip lands
-  // before its barrier, and the bf16 dZ of element v only covers float slots
-  // of elements < v)
+  // ---- pass 2: dZ in place, strip by strip (over fp32 logits every load of
+  // a strip lands before its barrier, and the bf16 dZ of element v only
+  // covers float slots of elements < v; over bf16 logits each thread
+  // overwrites only what it has just read)
   for (int64_t base = 0; base < ngroups; base += kStrip) {
     Load4 xs[kUnroll], ys[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t g = base + u * kRowThreads + tid;
       if (g < ngroups) {
-        xs[u] = load_group_last(Srow, g, V, true);
-        ys[u] = load_group_last(Trow, g, V, true);
+        xs[u] = sr.load_last(g, V);
+        ys[u] = tr.load_last(g, V);
       }
     }
-    __syncthreads();
+    if constexpr (!SB) __syncthreads();
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t g = base + u * kRowThreads + tid;
@@ -485,7 +538,7 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
         const JsdTerms j = jsd_terms(xs[u].v[i], ys[u].v[i], lse_s, lse_t);
         d[i] = coef * j.q * (0.5f * j.gq - half_b);
       }
-      if (a.dz_bf16) {
+      if (SB || a.dz_bf16) {
         if (e + 4 <= V) {
           uint2 pk;
           pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
@@ -505,7 +558,7 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
       }
     }
   }
-  if (a.dz_bf16) zero_pad(Zb, V, tid);
+  if (SB || a.dz_bf16) zero_pad(Zb, V, tid);
 }
 
 __global__ __launch_bounds__(1024) void prep_kernel(const int64_t *labels, int64_t BT,
@@ -664,16 +717,22 @@ void launch_prep(const int64_t *labels, int64_t BT, int64_t ignore_index, int he
                      head, reduction, V, sc);
 }
 
+template <bool SB>
+void launch_row_t(const RowArgs &a, hipStream_t st) {
+  if (a.head == HEAD_KL)
+    hipLaunchKernelGGL((row_kernel<HEAD_KL, SB>), dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else if (a.head == HEAD_SEL)
+    hipLaunchKernelGGL((row_kernel<HEAD_SEL, SB>), dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else if (a.head == HEAD_CE)
+    hipLaunchKernelGGL((row_kernel<HEAD_CE, SB>), dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else if (a.head == HEAD_JSD)
+    hipLaunchKernelGGL(jsd_row_kernel<SB>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+}
+
 void launch_row(const RowArgs &a, hipStream_t st) {
   if (a.rows <= 0) return;
-  if (a.head == HEAD_KL)
-    hipLaunchKernelGGL(row_kernel<HEAD_KL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
-  else if (a.head == HEAD_SEL)
-    hipLaunchKernelGGL(row_kernel<HEAD_SEL>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
-  else if (a.head == HEAD_CE)
-    hipLaunchKernelGGL(row_kernel<HEAD_CE>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(jsd_row_kernel, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  if (a.s_bf16) launch_row_t<true>(a, st);
+  else launch_row_t<false>(a, st);
 }
 
 void launch_colsum(const void *dZ, int dz_bf16, int64_t ldz, int64_t rows, int64_t V,

@@ -22,7 +22,7 @@ def to_np(t):
     return None if t is None else t.detach().cpu().double().numpy()
 
 
-def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0"):
+def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0", logits_bf16=False):
     import lm_head_projection_token_amd as fll
 
     def dev(t):
@@ -35,7 +35,7 @@ def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0"):
         temperature=case.temperature, eps=case.eps, compute_dW=case.compute_dW,
         compute_db=case.compute_db, chunk_rows=chunk_rows, per_row=per_row,
         X_teacher=dev(inp.get("X_teacher")), W_teacher=dev(inp.get("W_teacher")),
-        b_teacher=dev(inp.get("b_teacher")))
+        b_teacher=dev(inp.get("b_teacher")), logits_bf16=logits_bf16)
     torch.cuda.synchronize()
     return out
 
@@ -80,14 +80,42 @@ def check_grad(got, ref, dtype: str, what: str):
         assert np.abs(got).max() == 0.0, f"{what}: expected exact zeros"
 
 
-def compare_full(out, ref, case):
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
+def logit_rounding_bound(inp, case, rows=None):
+    """Per-row bound on how far rounding the chunk logits to bf16 can move a
+    per-row loss term, to first order: every logit moves by at most
+    u |S_rv| (u = 2^-8), and each head's term has a logit gradient whose
+    absolute row sum is at most 2 (the label's logit and the log-sum-exp; the
+    target's logits and the log-sum-exp; for JSD the same for each side), so
+    |d L_r| <= 2 u (max_v |S_rv| + max_v |T_rv|) with T the teacher's logits."""
+    def row_max(X, W, b):
+        X = X.double() if rows is None else X[rows].double()
+        S = X @ W.double().T
+        if b is not None:
+            S = S + b.double()
+        return (S / case.temperature).abs().max(dim=1).values.numpy()
+
+    m = row_max(inp["X"], inp["W"], inp["b"])
+    if inp.get("X_teacher") is not None:
+        m = m + row_max(inp["X_teacher"], inp["W_teacher"], inp.get("b_teacher"))
+    return 2.0 * BF16_UNIT_ROUNDOFF * m
+
+
+def compare_full(out, ref, case, per_row_atol=None):
+    """Loss and gradients at the stated tolerances; per-row terms at the
+    loss tolerance, plus per_row_atol (a per-row array) when given."""
     check_loss(float(out["loss"]), ref["loss"], case.dtype)
     if out.get("per_row") is not None:
         per = to_np(out["per_row"])
         tol = 1e-5 if case.dtype == "fp32" else 2e-3
         scale = float(np.abs(ref["per_row"]).max()) if ref["per_row"].size else 0.0
-        np.testing.assert_allclose(per, ref["per_row"], rtol=tol, atol=tol * scale,
-                                   err_msg="per_row")
+        atol = tol * scale if per_row_atol is None else tol * scale + per_row_atol
+        err = np.abs(per - ref["per_row"])
+        bad = err > atol + tol * np.abs(ref["per_row"])
+        assert not bad.any(), \
+            f"per_row: {int(bad.sum())} rows out of tolerance, max err {err.max():.3e}"
     check_grad(to_np(out["dX"]), ref["dX"], case.dtype, "dX")
     if case.compute_dW:
         check_grad(to_np(out["dW"]), ref["dW"], case.dtype, "dW")

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(fll.LIB_PATH)
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert fll.fll_version() == 2
+    assert fll.fll_version() == 3
     out = subprocess.run(["nm", "-D", "--defined-only", fll.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fll_\w+)", out))
@@ -160,6 +160,8 @@ def test_plan_empty_batch():
     (dict(head="jsd", H_teacher=4096, teacher_has_bias=2), fll.FLL_ERR_INVALID_ARG),
     (dict(H_teacher=4096), fll.FLL_ERR_INVALID_ARG),              # teacher for another head
     (dict(teacher_has_bias=True), fll.FLL_ERR_INVALID_ARG),
+    (dict(logits_bf16=2), fll.FLL_ERR_INVALID_ARG),
+    (dict(logits_bf16=True, dtype="fp32"), fll.FLL_ERR_INVALID_ARG),  # bf16 problems only
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(fll.FllError) as e:
@@ -258,6 +260,21 @@ def test_plan_jsd_adds_the_teacher_chunk():
     extra = j.workspace_bytes - a.workspace_bytes
     assert extra >= j.chunk_rows * j.s_pitch * 4 + j.chunk_rows * j.stat_tiles * 8
     assert j.off_teacher_stats >= j.off_teacher + j.chunk_rows * j.s_pitch * 4
+
+
+@pytest.mark.parametrize("head,kw", [("selective", {}), ("kl", {}),
+                                     ("jsd", dict(H_teacher=2048))])
+def test_plan_bf16_logits_halve_the_chunk(head, kw):
+    # bf16 chunk logits: the same chunk size, 2 bytes per logit for the
+    # student's (and the teacher's) chunk instead of 4
+    f = fll.fll_plan(_prob(head=head, **kw))
+    h = fll.fll_plan(_prob(head=head, logits_bf16=True, **kw))
+    assert (h.chunk_rows, h.n_chunks, h.s_pitch, h.dx_splits) == \
+        (f.chunk_rows, f.n_chunks, f.s_pitch, f.dx_splits)
+    n_chunks = 2 if head == "jsd" else 1
+    saved = n_chunks * f.chunk_rows * f.s_pitch * 2
+    assert f.workspace_bytes - h.workspace_bytes == saved
+    assert h.off_rowval - h.off_logits >= h.chunk_rows * h.s_pitch * 2
 
 
 def test_fwd_bwd_rejects_edited_plan():

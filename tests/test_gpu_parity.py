@@ -74,6 +74,33 @@ def test_small_parity(name):
     H.compare_full(out, ref, case)
 
 
+BF16_SMALL = sorted(k for k, c in SMALL.items() if c.dtype == "bf16")
+
+
+@pytest.mark.parametrize("name", BF16_SMALL)
+def test_small_parity_bf16_logits(name):
+    # chunk logits kept in bf16: the same cases and the same loss and gradient
+    # tolerances; the per-row terms also allow for the logits' rounding
+    case = SMALL[name]
+    print(f"[parity bf16 logits] {name} {case}", flush=True)
+    inp = H.make(case)
+    H.compare_full(H.run_gpu(inp, case, logits_bf16=True), H.run_oracle(inp, case), case,
+                   per_row_atol=H.logit_rounding_bound(inp, case))
+
+
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
+def test_bf16_logits_dx_independent_of_gradient_flags(head):
+    # with bf16 chunk logits too, dX does not depend on compute_dW / compute_db
+    kw = dict(H_teacher=72) if head == "jsd" else {}
+    case = workloads.small_case(BT=600, H=136, V=1500, dtype="bf16", head=head,
+                                has_bias=True, ignore_frac=0.1, w_std=0.05, seed=23, **kw)
+    inp = H.make(case)
+    a = H.run_gpu(inp, case, logits_bf16=True)
+    b = H.run_gpu(inp, case.replace(compute_dW=True, compute_db=True), logits_bf16=True)
+    assert torch.equal(a["dX"], b["dX"])
+    assert torch.equal(a["loss"], b["loss"])
+
+
 def test_unnormalised_target():
     # target rows summing to 1.3: the exact gradient uses Q_r = sum_v q_rv
     case = workloads.small_case(BT=96, H=64, V=300, dtype="fp32", head="kl",
