@@ -11,8 +11,10 @@ the frozen lm_head GRPO page times (Details). ``--config 5`` selects the
 trainable KL distillation workload at the same H and V, ``--config jsd`` the
 Jensen-Shannon head against a teacher with its own H = 4096 projection.
 
-Prints one JSON line. ``roofline`` covers the dominant kernel, timed with
-HIP events on the library's stream over the timed steps; ``cpu_baseline``
+Prints one JSON line. ``value`` and ``ms_per_step`` come from the timed
+steps alone; ``kernels`` and ``roofline`` (the dominant kernel) from as many
+steps again with HIP events around every kernel on the library's stream, so
+the events' own cost stays out of the step time; ``cpu_baseline``
 times the CPU float64 oracle on a bounded row sample and extrapolates
 linearly in rows (every step of the method is row-local except the final
 sum).
@@ -203,7 +205,8 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    fll.fll_profile_enable(True)
+    # The steps themselves, with no per-kernel events (each event adds a few
+    # microseconds at a kernel boundary: ~10 % of a V=32000 step).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -214,9 +217,15 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # The same number of steps again with the library's HIP events around
+    # every kernel, on its launch stream: the per-kernel times and roofline.
+    fll.fll_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     prof = fll.fll_profile_read(reset=True)
     fll.fll_profile_enable(False)
-    ms = ev0.elapsed_time(ev1) / args.steps
     if not torch.isfinite(loss):
         raise RuntimeError("non-finite loss")
 
