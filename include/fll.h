@@ -208,9 +208,9 @@ int fll_plan(const fll_problem *problem, size_t max_workspace_bytes,
  * [frozen lm_head GRPO page, Summary; LoRA normalization page, Key Changes].
  *
  * A non-ignored label outside [0, V) (SELECTIVE, CROSS_ENTROPY) is not a
- * memory error: that
- * row's per_row value and the loss become NaN and its dlogits are zero.
- * Calls that share a workspace must be ordered on one stream.
+ * memory error: that row's per_row value and the loss become NaN and its
+ * dlogits are zero. Calls that share a workspace must be ordered on one
+ * stream.
  *
  *   plan    host, from fll_plan, read only.
  *   args    host struct of device pointers, read only.

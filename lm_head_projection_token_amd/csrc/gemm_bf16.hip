@@ -294,16 +294,27 @@ struct EpiLogits {
   }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,
                                          int) const {
-    if (n + 4 <= nmax) {
-      store4_in(m, n, f32x4{v.x, v.y, v.z, v.w}, 0);
-    } else {
-      const float ve[4] = {v.x, v.y, v.z, v.w};
+    const float ve[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (B16) {
+      unsigned short *p = static_cast<unsigned short *>(S) + m * lds + n;
+      if (n + 4 <= nmax) {
+        uint2 pk;
+        pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
+        pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+        *reinterpret_cast<uint2 *>(p) = pk;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (n + e < nmax) {
-          if constexpr (B16) static_cast<unsigned short *>(S)[m * lds + n + e] = f2bf(ve[e]);
-          else static_cast<float *>(S)[m * lds + n + e] = ve[e];
-        }
+        for (int e = 0; e < 4; ++e)
+          if (n + e < nmax) p[e] = f2bf(ve[e]);
+      }
+    } else {
+      float *p = static_cast<float *>(S) + m * lds + n;
+      if (n + 4 <= nmax) {
+        *reinterpret_cast<float4 *>(p) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < nmax) p[e] = ve[e];
       }
     }
   }
