@@ -102,11 +102,11 @@ def test_plan_does_not_depend_on_gradient_flags():
 
 
 def test_plan_dx_split_fills_the_device():
-    # the vocabulary split of the dX GEMM targets ~512 workgroups of 256 x 256
-    # output tiles, keeps >= 2048 vocabulary entries per split, covers V
-    # exactly once, and does not depend on the gradient flags
-    for BT, V, want in ((8192, 128256, 2), (1024, 32000, 15), (300, 1000, 1),
-                        (600, 128256, 16)):
+    # the vocabulary split of the dX GEMM targets one workgroup of 256 x 256
+    # output tiles per CU (256), keeps >= 2048 vocabulary entries per split,
+    # covers V exactly once, and does not depend on the gradient flags
+    for BT, V, want in ((8192, 128256, 1), (4096, 128256, 2), (1024, 32000, 8),
+                        (300, 1000, 1), (600, 128256, 8), (256, 32000, 15)):
         for flags in (dict(), dict(compute_dW=True, has_bias=True, compute_db=True)):
             pl = fll.fll_plan(_prob(BT=BT, V=V, **flags))
             tiles = -(-pl.chunk_rows // 256) * (4096 // 256)
@@ -114,7 +114,8 @@ def test_plan_dx_split_fills_the_device():
             assert pl.dx_splits * pl.dx_split_len >= V
             assert (pl.dx_splits - 1) * pl.dx_split_len < V
             assert pl.dx_splits == 1 or V / pl.dx_splits >= 2048 - 64
-            assert pl.dx_splits * tiles >= 512 or pl.dx_splits == max(1, min(16, V // 2048))
+            assert pl.dx_splits * tiles >= 256 or pl.dx_splits == max(1, min(16, V // 2048))
+            assert pl.dx_splits == 1 or (pl.dx_splits - 1) * tiles < 256
 
 
 def test_plan_budget_shrinks_chunks_then_fails():

@@ -237,8 +237,8 @@ def test_chunk_size_does_not_change_dx():
 
 
 def test_chunk_size_changes_dx_only_by_reassociation():
-    # the vocabulary split of dX follows the chunk size (about 512 workgroups:
-    # 16 splits at C = 512, 11 at C = 768, 8 at C = 1024 here), so dX rows are
+    # the vocabulary split of dX follows the chunk size (one workgroup per CU:
+    # 8 splits at C = 512, 6 at C = 768, 4 at C = 1024 here), so dX rows are
     # fp32 sums in another order: equal to a bf16 rounding step; the per-row
     # loss terms do not depend on it
     case = workloads.small_case(BT=1024, H=4096, V=32768, dtype="bf16", head="selective",
