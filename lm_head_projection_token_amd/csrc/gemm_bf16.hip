@@ -13,8 +13,11 @@
 //
 // One kernel template serves all three. A workgroup of 256 threads (four
 // wavefronts in a 2 x 2 grid) computes a 256 x 256 tile; each wavefront owns
-// 128 x 128 of it as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 with fp32
-// accumulators (256 AGPRs).
+// 128 x 128 of it as 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 with fp32
+// accumulators (256 AGPRs). This shape, rather than 32 x 32 x 16 blocks,
+// because with random operands the chip's power limit sets the clock: an
+// MFMA-only loop held 2.07 GHz with 16 x 16 x 32 against 1.72-1.77 GHz with
+// 32 x 32 x 16 at the same issue rate (2.38 GHz for both on constant data).
 //
 // Staging. Each K-step of 32 moves a 256 x 32 slice of each operand from
 // global memory straight into LDS with buffer_load_dwordx4 ... lds (no
@@ -29,8 +32,8 @@
 //   chunks XOR-swizzled by K-row, read with ds_read_b64_tr_b16, whose
 //   16-lane transpose hands each lane four consecutive K-values of its own
 //   column; two such reads form one MFMA operand of eight K-values.
-// MFMA fragments are double-buffered in registers: the reads for the next
-// 16-deep half-step are issued between the MFMAs of the current one.
+// MFMA fragments are double-buffered in registers: the reads of the next
+// K-step's fragments are issued between the 64 MFMAs of the current one.
 //
 // Tile order. Workgroups are dispatched round-robin over the 8 XCDs. The
 // logical tile sequence walks groups of G tile-rows (or tile-columns), the
@@ -68,16 +71,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = FLL_GEMM_STAGES;
 constexpr int kThreads = 256;
+static_assert(NSTAGE % 2 == 0, "the K-steps alternate between two fragment register sets");
 constexpr int kOperandBytes = 256 * BK * 2;     // 16 KB per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;  // 32 KB
 constexpr int kLoadsPerStage = 8;               // per thread: 4 for A, 4 for B
-// Loads still in flight when stage s is needed: the later full stages, plus
-// the A half of the newest one (prologue: the later full stages only).
-constexpr int kVmcntLoop = kLoadsPerStage * (NSTAGE - 3) + kLoadsPerStage / 2;
-constexpr int kVmcntPrologue = kLoadsPerStage * (NSTAGE - 2);
-// Epilogue slab: 32 rows of the wave's 128 fp32 columns, rows 528 bytes apart.
+// Loads still in flight when a stage is needed: those of the two later
+// stages (when its fragments are read during K-step kt - 1, the stages of
+// K-steps kt + 1 and kt + 2; in the prologue, before the first reads, the
+// other NSTAGE - 1 stages).
+constexpr int kVmcntLoop = kLoadsPerStage * (NSTAGE - 2);
+constexpr int kVmcntPrologue = kLoadsPerStage * (NSTAGE - 1);
+// Epilogue slab: 16 rows of the wave's 128 fp32 columns, rows 528 bytes apart.
 constexpr int kSlabPitch = 132;                     // floats
-constexpr int kSlabBytes = 32 * kSlabPitch * 4;     // 16896 per wave
+constexpr int kSlabBytes = 16 * kSlabPitch * 4;     // 8448 per wave
 static_assert(4 * kSlabBytes + BN * 4 <= NSTAGE * kStageBytes,
               "epilogue slabs and bias table reuse the stages");
 constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
@@ -125,7 +131,7 @@ struct OpK {
   int64_t ld, row0, nrows;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
   int kc[4];         // their K offsets within the slice
-  unsigned fa[2];    // LDS addresses of the fragment reads (half-step 0 and 1)
+  unsigned fa;       // LDS address of this lane's fragment reads (block 0)
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
                                        int64_t nrows_, int wave, int lane, int wr,
@@ -141,12 +147,10 @@ struct OpK {
       voff[i] = unsigned((int64_t(r) * ld + 8 * c) * 2);
       kc[i] = 8 * c;
     }
-    const int r = wr + (lane & 31);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * h + (lane >> 5);
-      fa[h] = lds_base + unsigned(r * 64 + 16 * (c ^ swz_k(r)));
-    }
+    // lane l: row l % 16 of each 16-row block, K-values 8 (l / 16) .. + 7
+    const int r = wr + (lane & 15);
+    const int c = lane >> 4;
+    fa = lds_base + unsigned(r * 64 + 16 * (c ^ swz_k(r)));
   }
   // Load chunk i of this thread's share of the slice starting at K = k0 into
   // the stage at LDS byte offset `stage`. CHECK: the slice may end before
@@ -158,17 +162,18 @@ struct OpK {
     const unsigned v = (!CHECK || k0 + kc[i] < kend) ? voff[i] : kOOB;
     load_lds16(r, stage + (wave * 4 + i) * 1024, v);
   }
-  static constexpr int kReads = 4;  // LDS reads per half-step
-  // Read number X (0..3) of half-step H from the stage at LDS byte offset OFF:
-  // block X (rows wr + 32 X ...). The stage and block offsets are immediates.
-  template <int OFF, int X, int H>
-  __device__ __forceinline__ void read(bf16x8 (&f)[4]) const {
+  static constexpr int kReads = 8;  // LDS reads per K-step
+  // Read X (0..7) of the K-step in the stage at LDS byte offset OFF: block X
+  // (rows wr + 16 X ..; adding 16 rows leaves the swizzle unchanged). The
+  // stage and block offsets are instruction immediates.
+  template <int OFF, int X>
+  __device__ __forceinline__ void read(bf16x8 (&f)[8]) const {
     // the read offset field is 16 bits: whole 64 KB steps go into the base
     // (loop-invariant, so held in a register)
-    const unsigned base = fa[H] + unsigned(OFF >> 16) * 65536u;
+    const unsigned base = fa + unsigned(OFF >> 16) * 65536u;
     asm volatile("ds_read_b128 %0, %1 offset:%2"
                  : "=v"(f[X])
-                 : "v"(base), "i"(OFF % 65536 + X * 2048));
+                 : "v"(base), "i"(OFF % 65536 + X * 1024));
   }
 };
 
@@ -177,7 +182,7 @@ struct OpMN {
   const unsigned short *p;
   int64_t ld, col0;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (k0, col0)
-  unsigned fb[4];    // LDS addresses of the transpose reads, block i (half-step 0)
+  unsigned fb[8];    // LDS addresses of the transpose reads, block i
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t col0_,
                                        int wave, int lane, int wr, unsigned lds_base) {
@@ -190,13 +195,15 @@ struct OpMN {
       const int c = (lane & 31) ^ swz_mn(kr);
       voff[i] = unsigned((int64_t(kr) * ld + 8 * c) * 2);
     }
-    // 16-lane group G, lane q: K-row 8 (G >> 1) + (q >> 2), columns
-    // wr + 32 i + 16 (G & 1) + 4 (q & 3) .. + 3.
+    // 16-lane group G, lane q: K-row 8 G + (q >> 2), columns
+    // wr + 16 i + 4 (q & 3) .. + 3; after the transpose lane q holds column
+    // wr + 16 i + q, K-values 8 G .. + 3 (and + 4 .. + 7 from the K-rows four
+    // below, whose swizzle is the same).
     const int G = lane >> 4, q = lane & 15;
-    const int k = 8 * (G >> 1) + (q >> 2);
+    const int k = 8 * G + (q >> 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = wr + 32 * i + 16 * (G & 1) + 4 * (q & 3);
+    for (int i = 0; i < 8; ++i) {
+      const int col = wr + 16 * i + 4 * (q & 3);
       const int c = col >> 3, half = (col >> 2) & 1;
       fb[i] = lds_base + unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
     }
@@ -209,18 +216,18 @@ struct OpMN {
     const __amdgpu_buffer_rsrc_t r = rsrc(p + k0 * ld + col0, ((kend - k0) * ld - col0) * 2);
     load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
   }
-  static constexpr int kReads = 8;  // LDS reads per half-step
-  // Read number X (0..7) of half-step H from the stage at LDS byte offset
-  // OFF: block X / 2, K-values 4 (X % 2) .. + 3 of each lane's eight (the two
-  // halves of the MFMA operand).
-  template <int OFF, int X, int H>
-  __device__ __forceinline__ void read(bf16x8 (&f)[4]) const {
+  static constexpr int kReads = 16;  // LDS reads per K-step
+  // Read X (0..15) of the K-step in the stage at LDS byte offset OFF: block
+  // X / 2, K-values 4 (X % 2) .. + 3 of each lane's eight (the two halves of
+  // the MFMA operand).
+  template <int OFF, int X>
+  __device__ __forceinline__ void read(bf16x8 (&f)[8]) const {
     constexpr int i = X >> 1;
     const unsigned base = fb[i] + unsigned(OFF >> 16) * 65536u;
     i16x4 v;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
                  : "=v"(v)
-                 : "v"(base), "i"(OFF % 65536 + H * 16 * 512 + (X & 1) * 4 * 512));
+                 : "v"(base), "i"(OFF % 65536 + (X & 1) * 4 * 512));
     auto w = __builtin_bit_cast(i16x8, f[i]);
     if constexpr (X & 1) {
       w = __builtin_shufflevector(w, __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1),
@@ -407,13 +414,13 @@ struct EpiDw {
 };
 
 // The inner loop's MFMAs and LDS fragment reads are volatile inline assembly,
-// so they issue in exactly the order written: each half-step interleaves the
-// reads of the next half-step's fragments and a quarter of the next stage's
-// loads with its 16 MFMAs. The compiler neither sees the reads' latency nor
+// so they issue in exactly the order written: each K-step interleaves the
+// reads of the next K-step's fragments and the loads of a new stage with
+// its 64 MFMAs. The compiler neither sees the reads' latency nor
 // treats the asm as MFMAs, so the LDS waits are explicit and the accumulators
 // rest a few cycles before the epilogue reads them.
-__device__ __forceinline__ void mfma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // max of three floats (v_max3_f32). fmaxf on values read from accumulator
 // registers would first quiet each input with an extra v_max_f32 copy.
@@ -481,23 +488,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   if constexpr (B_K) opb.init(d.B, d.ldb, n0, d.N, wave, lane, wn * 128, lds_base + kOperandBytes);
   else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128, lds_base + kOperandBytes);
 
-  f32x16 acc[4][4];
+  // acc[i][j]: the 16 x 16 block of rows wm * 128 + 16 i, columns wn * 128 + 16 j
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][k][e] = 0.0f;
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // K-step kt (the last one may be partial) computes from stage kt % NSTAGE
-  // and loads the slice of K-step kt + NSTAGE - 1. The loop is unrolled by
-  // NSTAGE, so every stage offset below is a compile-time constant.
+  // K-step kt (the last one may be partial) multiplies the fragments of
+  // slice kt, held in registers; meanwhile it reads the fragments of slice
+  // kt + 1 from its stage into the other register set and loads slice
+  // kt + NSTAGE into the stage slice kt occupied. The loop is unrolled by
+  // NSTAGE (even), so every stage offset and register set below is a
+  // compile-time constant.
   const int nkt = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
   const int nkt_full = kend > kbeg ? int((kend - kbeg) / BK) : 0;
 
+  bf16x8 fa[2][8], fb[2][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    fa[0][i] = fa[1][i] = bf16x8{};
+    fb[0][i] = fb[1][i] = bf16x8{};
+  }
   if (nkt > 0) {
-    // prologue: NSTAGE - 1 stages in flight, wait for the first
-    static_for<NSTAGE - 1>([&](auto S) __attribute__((always_inline)) {
+    // prologue: all NSTAGE stages in flight; wait for the first, read it
+    static_for<NSTAGE>([&](auto S) __attribute__((always_inline)) {
       constexpr int s = decltype(S)::value;
       const int64_t k0 = kbeg + int64_t(s) * BK;
 #pragma unroll
@@ -508,98 +523,77 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     });
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntPrologue) : "memory");
     __builtin_amdgcn_s_barrier();
-  }
-
-  bf16x8 fa[2][4], fb[2][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[0][i] = fa[1][i] = bf16x8{};
-    fb[0][i] = fb[1][i] = bf16x8{};
-  }
-  if (nkt > 0) {
     static_for<OA::kReads>([&](auto X) __attribute__((always_inline)) {
-      opa.template read<0, decltype(X)::value, 0>(fa[0]);
+      opa.template read<0, decltype(X)::value>(fa[0]);
     });
     static_for<OB::kReads>([&](auto X) __attribute__((always_inline)) {
-      opb.template read<0, decltype(X)::value, 0>(fb[0]);
+      opb.template read<0, decltype(X)::value>(fb[0]);
     });
   }
-
-  // One half-step: 16 MFMAs on (ca, cb); between them the reads of (na, nb)
-  // (half-step H of the stage at offset OFF) and, after MFMAs 0, 4, 8, 12,
-  // one staging load each.
-  auto half = [&](auto OFF_, auto H_, bf16x8(&ca)[4], bf16x8(&cb)[4], bf16x8(&na)[4],
-                  bf16x8(&nb)[4], auto &&load) __attribute__((always_inline)) {
-    constexpr int OFF = decltype(OFF_)::value, H = decltype(H_)::value;
-    constexpr int ea = 16 / OA::kReads, eb = 16 / OB::kReads;
-    static_for<16>([&](auto X_) __attribute__((always_inline)) {
-      constexpr int x = decltype(X_)::value;
-      mfma(acc[x >> 2][x & 3], cb[x & 3], ca[x >> 2]);
-      if constexpr (x % ea == 0) opa.template read<OFF, x / ea, H>(na);
-      if constexpr (x % eb == eb / 2) opb.template read<OFF, x / eb, H>(nb);
-      if constexpr ((x & 3) == 0) load(x >> 2);
-    });
-  };
 
   auto kstep = [&](auto U_, auto CHECK_, int kt) __attribute__((always_inline)) {
     constexpr int u = decltype(U_)::value;
     constexpr bool CHECK = decltype(CHECK_)::value;
-    constexpr int s_cur = u * kStageBytes;
-    constexpr int s_nxt = ((u + 1) % NSTAGE) * kStageBytes;
-    constexpr int s_pre = ((u + NSTAGE - 1) % NSTAGE) * kStageBytes;
-    const int64_t k_next = kbeg + int64_t(kt + NSTAGE - 1) * BK;
-    // [B] half-step 0 of stage kt; read half-step 1 of stage kt; request the
-    // A slice of K-step kt + NSTAGE - 1 (past the end: zero-filled, unread).
-    wait_lds();
-    half(std::integral_constant<int, s_cur>{}, std::integral_constant<int, 1>{}, fa[0], fb[0],
-         fa[1], fb[1], [&](int q) __attribute__((always_inline)) {
-           opa.template issue_one<CHECK>(lds + s_pre, wave, q, k_next, kend);
-         });
-    // [C] stage kt + 1 complete in LDS for every wave: of the loads issued so
-    // far only the later stages (8 per thread each) and the A half of K-step
-    // kt + NSTAGE - 1 (4) may still be in flight.
+    constexpr int cur = u & 1, nxt = cur ^ 1;
+    constexpr int s_nxt = ((u + 1) % NSTAGE) * kStageBytes;  // slice kt + 1
+    constexpr int s_cur = u * kStageBytes;                   // slice kt, free now
+    const int64_t k_load = kbeg + int64_t(kt + NSTAGE) * BK;
+    // Slice kt + 1 is in LDS for every wave, and every wave has its slice-kt
+    // fragments (so the stage of slice kt can be refilled): of this thread's
+    // loads only those of slices kt + 2 and kt + 3 may still be in flight.
     wait_lds();
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntLoop) : "memory");
     __builtin_amdgcn_s_barrier();
-    // [D] half-step 1 of stage kt; read half-step 0 of stage kt + 1; request
-    // the B slice of K-step kt + NSTAGE - 1.
-    half(std::integral_constant<int, s_nxt>{}, std::integral_constant<int, 0>{}, fa[1], fb[1],
-         fa[0], fb[0], [&](int q) __attribute__((always_inline)) {
-           opb.template issue_one<CHECK>(lds + s_pre + kOperandBytes, wave, q, k_next, kend);
-         });
+    // 64 MFMAs; between them the reads of slice kt + 1 and the 8 loads of
+    // slice kt + NSTAGE (4 of A, then 4 of B).
+    constexpr int ea = 64 / OA::kReads, eb = 64 / OB::kReads;
+    static_for<64>([&](auto X_) __attribute__((always_inline)) {
+      constexpr int x = decltype(X_)::value;
+      mfma(acc[x >> 3][x & 7], fb[cur][x & 7], fa[cur][x >> 3]);
+      if constexpr (x % ea == 0) opa.template read<s_nxt, x / ea>(fa[nxt]);
+      if constexpr (x % eb == eb / 2) opb.template read<s_nxt, x / eb>(fb[nxt]);
+      if constexpr ((x & 7) == 4) {
+        constexpr int q = x >> 3;
+        if constexpr (q < 4)
+          opa.template issue_one<CHECK>(lds + s_cur, wave, q, k_load, kend);
+        else
+          opb.template issue_one<CHECK>(lds + s_cur + kOperandBytes, wave, q - 4, k_load, kend);
+      }
+    });
   };
 
-  // Full-speed steps: the slice each one requests lies wholly before kend.
-  const int fast_end = nkt_full - (NSTAGE - 1);
+  // Full-speed steps: the slice each one loads lies wholly before kend.
+  const int fast_end = nkt_full - NSTAGE;
   int kt = 0;
   for (; kt + NSTAGE <= fast_end; kt += NSTAGE)
     static_for<NSTAGE>([&](auto U) __attribute__((always_inline)) {
       kstep(U, std::false_type{}, kt + decltype(U)::value);
     });
-  // The last steps request partial or empty slices.
+  // The last steps load partial or empty slices.
   for (; kt < nkt; kt += NSTAGE)
     static_for<NSTAGE>([&](auto U) __attribute__((always_inline)) {
       if (kt + decltype(U)::value < nkt) kstep(U, std::true_type{}, kt + decltype(U)::value);
     });
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  // The MFMAs take the B fragment as their first operand, so each 32 x 32
+  // The MFMAs take the B fragment as their first operand, so each 16 x 16
   // accumulator block holds the transposed product: lane l owns output row
-  // m = l % 32 of the block, and register r holds column
-  // 8 (r / 4) + 4 (l / 32) + r % 4. A lane therefore owns, for each of its
-  // four rows, 64 of the wave's 128 columns in runs of four, and lane l ^ 32
-  // owns the other 64.
+  // m = l % 16 of the block and its four consecutive columns
+  // 4 (l / 16) .. + 3, so acc[i][j] of lane l is row 16 i + l % 16,
+  // columns 16 j + 4 (l / 16) .. + 3 of the wave's 128 x 128. Lanes l, l ^ 16,
+  // l ^ 32 and l ^ 48 share a row.
   //
-  // Stored as they lie, a 64-lane store would write 32 rows x 32 bytes, a
-  // quarter of a cache line per row; the write path then runs far below its
-  // rate. So each 32-row slab of the wave's tile passes through LDS (the
-  // staging buffers are idle now): written in the accumulator layout, read
-  // back so that one instruction covers two rows x 128 columns, i.e. 512
-  // contiguous bytes per row. Rows of the slab sit 528 bytes apart in LDS,
-  // which spreads both the writes and the reads over all banks.
+  // Stored as they lie, a 64-lane store would write 16 rows x 64 bytes, half
+  // a cache line per row; the write path then runs far below its rate. So
+  // each 16-row slab of the wave's tile passes through LDS (the staging
+  // buffers are idle now): written in the accumulator layout, read back so
+  // that one instruction covers two rows x 128 columns, i.e. 512 contiguous
+  // bytes per row. Rows of the slab sit 528 bytes apart in LDS, which spreads
+  // both the writes and the reads over all banks.
   __syncthreads();  // every wave is done reading the staging buffers
   // The bias of the tile's 256 columns (0 past N) goes to LDS after the four
-  // slabs: read per slab, it is not held in registers across the epilogue.
+  // waves' slabs: read per slab, it is not held in registers across the
+  // epilogue.
   LDS_AS float *btab = (LDS_AS float *)(lds + 4 * kSlabBytes);
   if constexpr (Epi::kRowStats) {
     if (epi.bias) {
@@ -608,8 +602,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     }
   }
   LDS_AS float *slab = (LDS_AS float *)(lds + wave * kSlabBytes);
-  const int lrow = lane & 31;
-  const int lcol = 4 * (lane >> 5);
+  const int lrow = lane & 15;
+  const int lcol = 4 * (lane >> 4);
   const int crow = lane >> 5;        // coalesced layout: row 2 j + crow of the slab,
   const int ccol = 4 * (lane & 31);  // columns ccol .. ccol + 3 of the wave's 128
   const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
@@ -621,17 +615,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 
   // dW: the old values of slabs i and i + 1 are in flight while slab i is
   // transposed and stored.
-  f32x4 old[2][16];
-  auto load_old = [&](int i, f32x4(&o)[16]) __attribute__((always_inline)) {
+  f32x4 old[2][8];
+  auto load_old = [&](int i, f32x4(&o)[8]) __attribute__((always_inline)) {
     if constexpr (Epi::kReadModifyWrite) {
-      int64_t mrow = mw + i * 32 + crow;
+      int64_t mrow = mw + i * 16 + crow;
       asm volatile("" : "+v"(mrow));
       if (interior) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[j] = epi.load4_in(mrow + 2 * j, nw + ccol);
+        for (int j = 0; j < 8; ++j) o[j] = epi.load4_in(mrow + 2 * j, nw + ccol);
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 8; ++j) {
           const float4 t = mrow + 2 * j < d.M ? epi.load4(mrow + 2 * j, nw + ccol, d.N)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
           o[j] = f32x4{t.x, t.y, t.z, t.w};
@@ -644,84 +638,81 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     load_old(1, old[1]);
   }
 
-  // One 32-row slab; I is a compile-time constant so that acc[I] stays in
+  // One 16-row slab; I is a compile-time constant so that acc[I] stays in
   // registers (a runtime index would move the accumulators to scratch).
   auto do_slab = [&](auto I_) __attribute__((always_inline)) {
     constexpr int i = decltype(I_)::value;
     // keep each slab's register working set to itself
     __builtin_amdgcn_sched_barrier(0);
-    // this lane's 64 values of the slab: v[4 k + q] = columns k * 32 + 8 q + lcol + 0..3
-    f32x4 v[16];
+    // this lane's 32 values of the slab: v[j] = columns 16 j + lcol + 0..3
+    f32x4 v[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int j = 0; j < 8; ++j) v[j] = acc[i][j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[4 * k + q] = f32x4{acc[i][k][4 * q + 0], acc[i][k][4 * q + 1], acc[i][k][4 * q + 2],
-                             acc[i][k][4 * q + 3]};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) asm volatile("" : "+v"(v[c]));  // copied here, not earlier
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(v[j]));  // copied here, not earlier
     if constexpr (Epi::kRowStats) {
       // S = (acc + b) / tau, then this row's max and sum of exp over the
-      // wave's 128 columns below N, merged with lane l ^ 32.
-      const int64_t m = mw + i * 32 + lrow;
+      // wave's 128 columns below N, merged over the four lanes of the row.
+      const int64_t m = mw + i * 16 + lrow;
       if (epi.bias) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          const f32x4 b =
-              *(const LDS_AS f32x4 *)(btab + wn * 128 + (c >> 2) * 32 + 8 * (c & 3) + lcol);
-          v[c] = (v[c] + b) * epi.inv_tau;
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 b = *(const LDS_AS f32x4 *)(btab + wn * 128 + 16 * j + lcol);
+          v[j] = (v[j] + b) * epi.inv_tau;
         }
       } else if (epi.inv_tau != 1.0f) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) v[c] *= epi.inv_tau;
+        for (int j = 0; j < 8; ++j) v[j] *= epi.inv_tau;
       }
       if (epi.stats) {
-        // column of element e of v[c]: nw + (c >> 2) * 32 + 8 (c & 3) + lcol + e
+        // column of element e of v[j]: nw + 16 j + lcol + e
         float mx = -INFINITY;
         if (full) {
 #pragma unroll
-          for (int c = 0; c < 16; ++c) mx = max3(max3(mx, v[c].x, v[c].y), v[c].z, v[c].w);
+          for (int j = 0; j < 8; ++j) mx = max3(max3(mx, v[j].x, v[j].y), v[j].z, v[j].w);
         } else {
 #pragma unroll
-          for (int c = 0; c < 16; ++c)
+          for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (nw + (c >> 2) * 32 + 8 * (c & 3) + lcol + e < d.N) mx = fmaxf(mx, v[c][e]);
+              if (nw + 16 * j + lcol + e < d.N) mx = fmaxf(mx, v[j][e]);
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         // exp(v - mx) = 2^(v log2(e) - mx log2(e))
         const float off = mx == -INFINITY ? 0.0f : -mx * kLog2e;
         float se = 0.0f;
         if (full) {
 #pragma unroll
-          for (int c = 0; c < 16; ++c)
+          for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f(fmaf(v[c][e], kLog2e, off));
+            for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
         } else if (mx != -INFINITY) {
 #pragma unroll
-          for (int c = 0; c < 16; ++c)
+          for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (nw + (c >> 2) * 32 + 8 * (c & 3) + lcol + e < d.N)
-                se += __builtin_amdgcn_exp2f(fmaf(v[c][e], kLog2e, off));
+              if (nw + 16 * j + lcol + e < d.N)
+                se += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
         }
+        se += __shfl_xor(se, 16, 64);
         se += __shfl_xor(se, 32, 64);
-        if (lane < 32 && m < d.M && nw < d.N)
+        if (lane < 16 && m < d.M && nw < d.N)
           epi.stats[m * epi.n_stat + (nw >> 7)] = make_float2(mx, se);
       }
     }
 
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-      *(LDS_AS f32x4 *)(slab + lrow * kSlabPitch + (c >> 2) * 32 + 8 * (c & 3) + lcol) = v[c];
+    for (int j = 0; j < 8; ++j)
+      *(LDS_AS f32x4 *)(slab + lrow * kSlabPitch + 16 * j + lcol) = v[j];
     // A wave's LDS operations complete in order, so the reads see the writes;
-    // all sixteen are issued before the first store waits for them.
-    f32x4 rd[16];
+    // all eight are issued before the first store waits for them.
+    f32x4 rd[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < 8; ++j)
       rd[j] = *(const LDS_AS f32x4 *)(slab + (2 * j + crow) * kSlabPitch + ccol);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 8; ++j) {
       if constexpr (Epi::kReadModifyWrite) {
         rd[j].x += old[i & 1][j].x;
         rd[j].y += old[i & 1][j].y;
@@ -729,26 +720,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
         rd[j].w += old[i & 1][j].w;
       }
     }
-    int64_t mrow = mw + i * 32 + crow;
+    int64_t mrow = mw + i * 16 + crow;
     asm volatile("" : "+v"(mrow));  // row addresses are formed here, per slab
     if (interior) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) epi.store4_in(mrow + 2 * j, nw + ccol, rd[j], split);
+      for (int j = 0; j < 8; ++j) epi.store4_in(mrow + 2 * j, nw + ccol, rd[j], split);
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < 8; ++j)
         if (mrow + 2 * j < d.M)
           epi.store4(mrow + 2 * j, nw + ccol, d.N,
                      make_float4(rd[j].x, rd[j].y, rd[j].z, rd[j].w), split);
     }
     if constexpr (Epi::kReadModifyWrite) {
-      if constexpr (i + 2 < 4) load_old(i + 2, old[i & 1]);
+      if constexpr (i + 2 < 8) load_old(i + 2, old[i & 1]);
     }
   };
-  do_slab(std::integral_constant<int, 0>{});
-  do_slab(std::integral_constant<int, 1>{});
-  do_slab(std::integral_constant<int, 2>{});
-  do_slab(std::integral_constant<int, 3>{});
+  static_for<8>([&](auto I) __attribute__((always_inline)) { do_slab(I); });
 }
 
 inline int cdiv(int64_t a, int64_t b) { return int((a + b - 1) / b); }
