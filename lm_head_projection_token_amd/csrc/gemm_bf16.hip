@@ -91,12 +91,14 @@ constexpr unsigned kMaxRecords = 0x7fffffffu;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
 
 // Swizzles of the 16-byte chunk index. K-contiguous tiles (4 chunks per row):
-// the 32 rows that one ds_read_b128 touches spread over all banks.
-// MN-contiguous tiles (32 chunks per K-row): the four K-rows that a 16-lane
-// group of ds_read_b64_tr_b16 touches land on distinct banks.
+// the 16 rows that 16 lanes of one ds_read_b128 touch spread over all banks.
+// MN-contiguous tiles (32 chunks per K-row): a 16-lane group of
+// ds_read_b64_tr_b16 touches four K-rows k .. k + 3 and the group beside it
+// the four eight below, all at the same two chunks; {0, 10, 12, 6} by k & 3,
+// XOR 2 when k & 8, puts those eight K-rows on distinct banks.
 __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int swz_mn(int k) {
-  return (0x6ca0 >> ((k & 3) * 4)) & 15;  // {0, 10, 12, 6}[k & 3]
+  return ((0x6ca0 >> ((k & 3) * 4)) & 15) ^ ((k >> 2) & 2);  // {0, 10, 12, 6}[k & 3] ^ 2 [k & 8]
 }
 
 // Buffer descriptor of `bytes` bytes from `base` (clamped to [0, 2^31 - 1]).
@@ -121,25 +123,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
 }
 
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, LDS_AS void *dst,
-                                           unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+                                           unsigned voff, unsigned soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
 // ---- K-contiguous operand: element (row, k) at p[row * ld + k] -------------
 struct OpK {
   const unsigned short *p;
-  int64_t ld, row0, nrows;
+  int64_t ld, row0, nrows, kbeg;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
   int kc[4];         // their K offsets within the slice
   unsigned fa;       // LDS address of this lane's fragment reads (block 0)
+  __amdgpu_buffer_rsrc_t whole;  // the tile's rows from (row0, kbeg) to the end
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
-                                       int64_t nrows_, int wave, int lane, int wr,
-                                       unsigned lds_base) {
+                                       int64_t nrows_, int64_t kbeg_, int wave, int lane,
+                                       int wr, unsigned lds_base) {
     p = p_;
     ld = ld_;
     row0 = row0_;
     nrows = nrows_;
+    kbeg = kbeg_;
+    whole = rsrc(p + row0 * ld + kbeg, ((nrows - row0) * ld - kbeg) * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (wave * 4 + i) * 16 + (lane >> 2);
@@ -155,12 +160,20 @@ struct OpK {
   // Load chunk i of this thread's share of the slice starting at K = k0 into
   // the stage at LDS byte offset `stage`. CHECK: the slice may end before
   // k0 + BK, so chunks past kend are pointed outside the descriptor.
+  // Full slices (CHECK false) use one descriptor for the whole tile and
+  // step through K with the scalar offset: a row below nrows stays inside the
+  // descriptor at every k0 < K <= ld, and a row past it lies outside at every
+  // k0, whether or not the range check counts the scalar offset.
   template <bool CHECK>
   __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
                                             int64_t kend) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
-    const unsigned v = (!CHECK || k0 + kc[i] < kend) ? voff[i] : kOOB;
-    load_lds16(r, stage + (wave * 4 + i) * 1024, v);
+    if constexpr (CHECK) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
+      const unsigned v = k0 + kc[i] < kend ? voff[i] : kOOB;
+      load_lds16(r, stage + (wave * 4 + i) * 1024, v);
+    } else {
+      load_lds16(whole, stage + (wave * 4 + i) * 1024, voff[i], unsigned(k0 - kbeg) * 2u);
+    }
   }
   static constexpr int kReads = 8;  // LDS reads per K-step
   // Read X (0..7) of the K-step in the stage at LDS byte offset OFF: block X
@@ -483,9 +496,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   using OB = typename std::conditional<B_K, OpK, OpMN>::type;
   OA opa;
   OB opb;
-  if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, wave, lane, wm * 128, lds_base);
+  if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, kbeg, wave, lane, wm * 128, lds_base);
   else opa.init(d.A, d.lda, m0, wave, lane, wm * 128, lds_base);
-  if constexpr (B_K) opb.init(d.B, d.ldb, n0, d.N, wave, lane, wn * 128, lds_base + kOperandBytes);
+  if constexpr (B_K)
+    opb.init(d.B, d.ldb, n0, d.N, kbeg, wave, lane, wn * 128, lds_base + kOperandBytes);
   else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128, lds_base + kOperandBytes);
 
   // acc[i][j]: the 16 x 16 block of rows wm * 128 + 16 i, columns wn * 128 + 16 j
