@@ -10,7 +10,7 @@ The names mirror the C entry points: ``fll_plan``, ``fll_fwd_bwd``,
 convenience wrapper that allocates the outputs and the workspace with torch
 and calls ``fll_plan`` + ``fll_fwd_bwd``.
 
-The library must be built (``python -m lm_head_projection_token_amd.build``);
+The library must be built (``python lm_head_projection_token_amd/build.py``);
 importing this package without it raises, there is no fallback path.
 """
 
@@ -97,7 +97,7 @@ class FllError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m lm_head_projection_token_amd.build`")
+            f"{LIB_PATH} is not built; run `python lm_head_projection_token_amd/build.py`")
     # torch ships its own HIP and HSA runtimes. Loading torch first lets
     # libfll.so's libamdhip64.so.7 dependency resolve to torch's copy (same
     # soname), so the process holds one runtime; loaded the other way round,

@@ -1,6 +1,6 @@
 """Build ``libfll.so`` (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: ``python -m lm_head_projection_token_amd.build`` or ``build()``.
+Usage: ``python lm_head_projection_token_amd/build.py`` or ``build()``.
 Compiles every source under ``csrc/`` and links them into
 ``lm_head_projection_token_amd/libfll.so``. No GPU is needed: hipcc
 cross-compiles the gfx950 code objects.
