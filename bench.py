@@ -84,6 +84,47 @@ def row_bytes_per_valid_row(case, logits_bf16=False):
     return (s + extra + 2) * case.V
 
 
+def sample_clock(step, sync, samples=3):
+    """Average shader clock (GHz) while steps run back to back: `amd-smi
+    metric --clock` is read a few times from a helper thread, each reading
+    averaged over the GFX clock of every XCD. None if amd-smi is missing or
+    prints no GFX clock."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+
+    exe = shutil.which("amd-smi")
+    if not exe:
+        return None
+    readings = []
+    done = threading.Event()
+
+    def sampler():
+        try:
+            time.sleep(0.3)
+            for _ in range(samples):
+                out = subprocess.run([exe, "metric", "-g", "0", "--clock"], capture_output=True,
+                                     text=True, timeout=20).stdout
+                mhz = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+                if mhz:
+                    readings.append(sum(mhz) / len(mhz))
+        except Exception:  # pragma: no cover - a reading is optional
+            pass
+        finally:
+            done.set()
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + 60.0
+    while not done.is_set() and time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        sync()
+    th.join(timeout=30)
+    return sum(readings) / len(readings) / 1e3 if readings else None
+
+
 def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
     """Time the oracle on two row samples and extrapolate to the full batch."""
     import numpy as np
@@ -143,6 +184,8 @@ def main():
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--logits-bf16", action="store_true",
                     help="keep each chunk's logits in bf16 instead of fp32")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi shader-clock reading after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -269,6 +312,20 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_clock:
+        # The chip's power limit sets the shader clock under this load; the
+        # dense peak above assumes 2.4 GHz. Reported beside it, not instead.
+        print("[bench] reading the shader clock while steps run", file=sys.stderr, flush=True)
+        ghz = sample_clock(step, torch.cuda.synchronize)
+        if ghz:
+            peak_at_clock = PEAK_BF16_TFLOPS * ghz / 2.4 if case.dtype == "bf16" else \
+                PEAK_FP32_TFLOPS * ghz / 2.4
+            out["clock"] = {
+                "source": "amd-smi metric --clock (GFX clock averaged over the XCDs) while "
+                          "steps ran back to back after the timed region",
+                "GHz": ghz, "peak_at_clock": peak_at_clock,
+                "end_to_end_frac_at_clock": gemm_flops(case) / (ms / 1e3) / 1e12 / peak_at_clock,
+                "roofline_frac_at_clock": achieved / peak_at_clock}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, case)

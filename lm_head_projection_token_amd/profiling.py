@@ -7,6 +7,14 @@ Usage (from the repository root, after the rocprofv3 runs):
   python -m lm_head_projection_token_amd.profiling traffic \\
       --fetch DIR_F --write DIR_W --copy-fetch DIR_CF --copy-write DIR_CW \\
       --copy-bytes N --workload W --command "..." --out profiles/Y
+  python -m lm_head_projection_token_amd.profiling mfma \\
+      --dir DIR_M --workload W --command "..." --out profiles/Z
+
+The MFMA summary reads, per dispatch, SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE and GRBM_COUNT (one --pmc run
+with --kernel-trace, which gives each dispatch's duration) and reports the
+shader clock the kernel ran at, the MFMA pipes' busy fraction and the bf16
+MFMA flops counted by the hardware.
 
 The traffic summary reads FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of
 every library kernel, scales each counter by the factor that makes it read
@@ -143,6 +151,86 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_b
         fh.write("\n".join(lines))
 
 
+N_XCD = 8
+N_SIMD = 256 * 4
+PEAK_CLOCK_GHZ = 2.4
+FLOP_PER_CLK_SIMD_BF16 = 1024  # dense bf16: 256 CU x 4 SIMD x 1024 x 2.4 GHz = 2516.6 TFLOP/s
+
+
+def _trace_durations(d: str):
+    """{dispatch id: (kernel name, duration in ns)} from a kernel trace."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_trace.csv under {d}")
+    out = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out[int(r["Dispatch_Id"])] = (
+                    r["Kernel_Name"], float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    return out
+
+
+def mfma_summary(d, workload, command, out_base) -> None:
+    """Per kernel kind (median over dispatches): duration, shader clock
+    (GRBM_COUNT per XCD over the duration), busy clock (GRBM_GUI_ACTIVE per
+    XCD), MFMA busy fraction of every SIMD's active cycles, and the bf16 MFMA
+    flops the hardware counted, as TFLOP/s and as fractions of the dense peak
+    at 2.4 GHz and at the measured clock."""
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE",
+             "GRBM_COUNT")
+    vals = defaultdict(lambda: defaultdict(float))
+    for r in _counter_rows(d):
+        n = r["Counter_Name"]
+        if n in names:
+            vals[int(r["Dispatch_Id"])][n] += float(r["Counter_Value"])
+    durs = _trace_durations(d)
+    per_kind = defaultdict(list)
+    for did, c in vals.items():
+        if did not in durs or any(n not in c for n in names):
+            continue
+        kname, ns = durs[did]
+        kind = kernel_kind(kname)
+        if kind is None or ns <= 0:
+            continue
+        clk = c["GRBM_COUNT"] / N_XCD / ns          # cycles per ns = GHz
+        active = c["GRBM_GUI_ACTIVE"] / N_XCD
+        util = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * N_SIMD) if active else 0.0
+        tflops = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / ns / 1e3
+        peak_nominal = N_SIMD * FLOP_PER_CLK_SIMD_BF16 * PEAK_CLOCK_GHZ / 1e3
+        peak_clock = N_SIMD * FLOP_PER_CLK_SIMD_BF16 * clk / 1e3
+        per_kind[kind].append({"duration_ms": ns / 1e6, "clock_GHz": clk,
+                               "active_GHz": active / ns, "mfma_busy": util,
+                               "mfma_TFLOPs": tflops, "frac_peak": tflops / peak_nominal,
+                               "frac_peak_at_clock": tflops / peak_clock if clk else 0.0})
+    kinds = {}
+    for kind, rows in per_kind.items():
+        kinds[kind] = {k: statistics.median(r[k] for r in rows) for k in rows[0]}
+        kinds[kind]["dispatches"] = len(rows)
+    rec = {"workload": workload, "command": command, "src_sha256": source_hash(),
+           "kernels": kinds}
+    with open(out_base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = [f"# MFMA utilisation and shader clock: {workload}", "",
+             f"Command (from the repository root): `{command}`", "",
+             "Per dispatch: clock = GRBM_COUNT / 8 XCDs / duration; MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); bf16 "
+             "TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration (hardware-counted "
+             "MFMA flops, tail and padding included). Medians over dispatches; "
+             "durations are from the counter run, where dispatches are serialised.", "",
+             "| kernel | dispatches | duration (ms) | clock (GHz) | MFMA busy | "
+             "bf16 TFLOP/s | of peak at 2.4 GHz | of peak at the clock |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k, v in sorted(kinds.items(), key=lambda kv: -kv[1]["duration_ms"]):
+        lines.append(f"| {k} | {v['dispatches']} | {v['duration_ms']:.4f} | "
+                     f"{v['clock_GHz']:.3f} | {100 * v['mfma_busy']:.1f}% | "
+                     f"{v['mfma_TFLOPs']:.1f} | {100 * v['frac_peak']:.1f}% | "
+                     f"{100 * v['frac_peak_at_clock']:.1f}% |")
+    lines += ["", f"Kernel sources sha256: `{rec['src_sha256']}`", ""]
+    with open(out_base + ".md", "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -157,9 +245,14 @@ def main():
               "--command", "--out"):
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    m = sub.add_parser("mfma")
+    for a in ("--dir", "--workload", "--command", "--out"):
+        m.add_argument(a, required=True)
     args = ap.parse_args()
     if args.cmd == "kernels":
         kernels_summary(args.stats, args.workload, args.command, args.out, args.note)
+    elif args.cmd == "mfma":
+        mfma_summary(args.dir, args.workload, args.command, args.out)
     else:
         traffic_summary(args.fetch, args.write, args.copy_fetch, args.copy_write,
                         args.copy_bytes, args.workload, args.command, args.out)
