@@ -442,6 +442,33 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one output row of
+// a 16 x 16 block) with the gfx950 lane swaps: v_permlane16_swap exchanges
+// rows of 16 lanes pairwise and v_permlane32_swap the two halves, so after a
+// swap of a value with itself the two results hold x[l] and x[l ^ 16] (or
+// x[l ^ 32]) in every lane, in either order. VALU only: no LDS round trip
+// as a ds_bpermute would take.
+__device__ __forceinline__ float quad_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <bool A_K, bool B_K, class Epi>
@@ -682,8 +709,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
         // column of element e of v[j]: nw + 16 j + lcol + e
         float mx = -INFINITY;
         if (full) {
+          // two independent chains of max3
+          float ma = max3(v[0].x, v[0].y, v[0].z), mb = max3(v[1].x, v[1].y, v[1].z);
+          ma = max3(ma, v[0].w, v[2].x);
+          mb = max3(mb, v[1].w, v[3].x);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) mx = max3(max3(mx, v[j].x, v[j].y), v[j].z, v[j].w);
+          for (int j = 2; j < 8; j += 2) {
+            ma = max3(ma, v[j].y, v[j].z);
+            mb = max3(mb, v[j + 1].y, v[j + 1].z);
+            ma = j + 2 < 8 ? max3(ma, v[j].w, v[j + 2].x) : vmax(ma, v[j].w);
+            mb = j + 3 < 8 ? max3(mb, v[j + 1].w, v[j + 3].x) : vmax(mb, v[j + 1].w);
+          }
+          mx = vmax(ma, mb);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -691,16 +728,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
             for (int e = 0; e < 4; ++e)
               if (nw + 16 * j + lcol + e < d.N) mx = fmaxf(mx, v[j][e]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = quad_max(mx);
         // exp(v - mx) = 2^(v log2(e) - mx log2(e))
         const float off = mx == -INFINITY ? 0.0f : -mx * kLog2e;
         float se = 0.0f;
         if (full) {
+          // four independent sums (one per element of the 4-column group)
+          float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) se += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
+            for (int e = 0; e < 4; ++e) s4[e] += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
+          se = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         } else if (mx != -INFINITY) {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -709,8 +748,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
               if (nw + 16 * j + lcol + e < d.N)
                 se += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
         }
-        se += __shfl_xor(se, 16, 64);
-        se += __shfl_xor(se, 32, 64);
+        se = quad_sum(se);
         if (lane < 16 && m < d.M && nw < d.N)
           epi.stats[m * epi.n_stat + (nw >> 7)] = make_float2(mx, se);
       }
