@@ -19,19 +19,29 @@
 // MFMA-only loop held 2.07 GHz with 16 x 16 x 32 against 1.72-1.77 GHz with
 // 32 x 32 x 16 at the same issue rate (2.38 GHz for both on constant data).
 //
-// Staging. Each K-step of 32 moves a 256 x 32 slice of each operand from
-// global memory straight into LDS with buffer_load_dwordx4 ... lds (no
-// registers, no LDS write instructions). Four LDS stages of 32 KB are in
-// flight, so a slice is requested about two and a half K-steps before its
-// MFMAs run. The buffer descriptors give zero fill for rows past the end of
-// an operand; K-chunks past the end are pointed outside the descriptor's
-// range and read as zero as well.
-//   K-contiguous operands keep their memory layout in LDS: 256 rows of 64
-//   bytes, 16-byte chunks XOR-swizzled by row, read with ds_read_b128.
-//   MN-contiguous operands also keep their layout: 32 K-rows of 512 bytes,
-//   chunks XOR-swizzled by K-row, read with ds_read_b64_tr_b16, whose
-//   16-lane transpose hands each lane four consecutive K-values of its own
-//   column; two such reads form one MFMA operand of eight K-values.
+// Staging. Each K-step of 32 consumes a 256 x 32 slice of each operand,
+// moved from global memory straight into LDS with buffer_load_dwordx4 ...
+// lds (no registers, no LDS write instructions). Four 16 KB slots per
+// operand (128 KB of LDS) hold four K-slices. The buffer descriptors give
+// zero fill for rows past the end of an operand; K-chunks past the end are
+// pointed outside the descriptor's range and read as zero as well.
+//   K-contiguous operands, when both are (the logits GEMM), are loaded a
+//   pair of slices at a time: one load instruction covers 8 rows x 128
+//   contiguous bytes (two slices of the same 8 rows, whole cache lines), so
+//   the texture path handles half the rows per instruction that single
+//   slices (16 rows x 64 bytes, half lines) would need; in LDS the slices of
+//   a pair sit 512 bytes apart inside 2 KB blocks of 8 rows, 16-byte chunks
+//   XOR-swizzled by row, read with ds_read_b128. A pair is loaded during the
+//   odd K-step that frees its two slots, about one and a half K-steps before
+//   its first slice is read.
+//   With an MN-contiguous partner (dX, dW) each K-step loads the slice four
+//   steps ahead, about two and a half K-steps before it is read; the
+//   K-contiguous operand then keeps 256 rows of 64 bytes per slot.
+//   MN-contiguous operands keep their memory layout: 32 K-rows of 512 bytes
+//   per slot (each load already covers whole lines), chunks XOR-swizzled by
+//   K-row, read with ds_read_b64_tr_b16, whose 16-lane transpose hands each
+//   lane four consecutive K-values of its own column; two such reads form one
+//   MFMA operand of eight K-values.
 // MFMA fragments are double-buffered in registers: the reads of the next
 // K-step's fragments are issued between the 64 MFMAs of the current one.
 //
@@ -72,15 +82,22 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = FLL_GEMM_STAGES;
 constexpr int kThreads = 256;
 static_assert(NSTAGE % 2 == 0, "the K-steps alternate between two fragment register sets");
-constexpr int kOperandBytes = 256 * BK * 2;     // 16 KB per operand per stage
-constexpr int kStageBytes = 2 * kOperandBytes;  // 32 KB
-constexpr int kLoadsPerStage = 8;               // per thread: 4 for A, 4 for B
-// Loads still in flight when a stage is needed: those of the two later
-// stages (when its fragments are read during K-step kt - 1, the stages of
-// K-steps kt + 1 and kt + 2; in the prologue, before the first reads, the
-// other NSTAGE - 1 stages).
-constexpr int kVmcntLoop = kLoadsPerStage * (NSTAGE - 2);
-constexpr int kVmcntPrologue = kLoadsPerStage * (NSTAGE - 1);
+static_assert(NSTAGE == 4, "two pairs of K-slices in flight");
+constexpr int kSliceBytes = 256 * BK * 2;       // 16 KB per operand per K-slice
+constexpr int kOperandBytes = NSTAGE * kSliceBytes;  // 64 KB per operand
+constexpr int kStageBytes = 2 * kSliceBytes;    // 32 KB of LDS per K-slice
+// Paired pipeline (both operands K-contiguous): K-slices are loaded in pairs
+// (2j, 2j + 1), each thread issuing 8 loads per operand per pair. A pair is
+// loaded during the odd K-step that frees its slots; at the top of an even
+// K-step the next pair may still be in flight.
+constexpr int kLoadsPerPair = 16;
+// Single pipeline (an MN-contiguous operand, whose loads already cover whole
+// cache lines): each K-step loads the slice NSTAGE steps ahead, 4 loads per
+// operand per thread; when a slice is needed the loads of the two later ones
+// may be in flight (in the prologue, of the other NSTAGE - 1).
+constexpr int kLoadsPerSlice = 8;
+constexpr int kVmcntLoop = kLoadsPerSlice * (NSTAGE - 2);
+constexpr int kVmcntPrologue = kLoadsPerSlice * (NSTAGE - 1);
 // Epilogue slab: 16 rows of the wave's 128 fp32 columns, rows 528 bytes apart.
 constexpr int kSlabPitch = 132;                     // floats
 constexpr int kSlabBytes = 16 * kSlabPitch * 4;     // 8448 per wave
@@ -128,12 +145,94 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, LDS_AS void
 }
 
 // ---- K-contiguous operand: element (row, k) at p[row * ld + k] -------------
-struct OpK {
+// LDS layout: 32 blocks of 8 rows, 2 KB each; inside a block the four K-slice
+// slots lie 512 bytes apart, each 8 rows x 64 bytes with the 16-byte chunks
+// XOR-swizzled by row. One load instruction covers one block of both slices
+// of a pair: lanes 0-31 the first slice, lanes 32-63 the second, i.e. 8 rows
+// x 128 contiguous bytes of global memory, whole cache lines.
+template <bool PAIRED>
+struct OpK;
+
+template <>
+struct OpK<true> {
+  const unsigned short *p;
+  int64_t ld, row0, nrows, kbeg;
+  unsigned voff[8];  // byte offsets of this thread's 8 pair chunks from (row0, k0)
+  int kc[2];         // their K offsets within the pair (by block parity)
+  unsigned fa;       // LDS address of this lane's fragment reads (block 0, slot 0)
+  __amdgpu_buffer_rsrc_t whole;  // the tile's rows from (row0, kbeg) to the end
+
+  __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
+                                       int64_t nrows_, int64_t kbeg_, int wave, int lane,
+                                       int wr, unsigned lds_base) {
+    p = p_;
+    ld = ld_;
+    row0 = row0_;
+    nrows = nrows_;
+    kbeg = kbeg_;
+    whole = rsrc(p + row0 * ld + kbeg, ((nrows - row0) * ld - kbeg) * 2);
+    // lane l of load i: row 8 (8 wave + i) + ((l >> 2) & 7), slice l >> 5 of
+    // the pair, chunk (l & 3) of the slot
+    const int h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (wave * 8 + i) * 8 + ((lane >> 2) & 7);
+      const int c = (lane & 3) ^ swz_k(r);
+      voff[i] = unsigned((int64_t(r) * ld + 32 * h + 8 * c) * 2);
+      if (i < 2) kc[i] = 32 * h + 8 * c;  // the swizzle repeats with the block parity
+    }
+    // lane l: row l % 16 of each 16-row block, K-values 8 (l / 16) .. + 7
+    const int r = wr + (lane & 15);
+    const int c = lane >> 4;
+    fa = lds_base + unsigned((r >> 3) * 2048 + (r & 7) * 64 + 16 * (c ^ swz_k(r)));
+  }
+  // Load block i of this thread's share of the pair of slices starting at
+  // K = k0 into the slots slot0, slot0 + 1 (`ops`: the operand's LDS base).
+  // CHECK: the pair may end before k0 + 2 BK, so chunks past kend are pointed
+  // outside the descriptor. Full pairs (CHECK false) use one descriptor for
+  // the whole tile and step through K with the scalar offset: a row below
+  // nrows stays inside the descriptor at every k0 < K <= ld, and a row past
+  // it lies outside at every k0, whether or not the range check counts the
+  // scalar offset.
+  template <bool CHECK>
+  __device__ __forceinline__ void issue_pair(LDS_AS char *ops, int slot0, int wave, int i,
+                                             int64_t k0, int64_t kend) const {
+    LDS_AS char *dst = ops + (wave * 8 + i) * 2048 + slot0 * 512;
+    if constexpr (CHECK) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
+      const unsigned v = k0 + kc[i & 1] < kend ? voff[i] : kOOB;
+      load_lds16(r, dst, v);
+    } else {
+      load_lds16(whole, dst, voff[i], unsigned(k0 - kbeg) * 2u);
+    }
+  }
+  // (named by the single pipeline's code, never called with this layout)
+  template <bool CHECK>
+  __device__ void issue_one(LDS_AS char *, int, int, int, int64_t, int64_t) const {
+    static_assert(CHECK && !CHECK, "paired layout: load pairs of slices");
+  }
+  static constexpr int kReads = 8;  // LDS reads per K-step
+  // Read X (0..7) of the K-step whose slice is in slot SLOT: block X (rows
+  // wr + 16 X ..; adding 16 rows leaves the swizzle unchanged). The slot and
+  // block offsets are instruction immediates.
+  template <int SLOT, int X>
+  __device__ __forceinline__ void read(bf16x8 (&f)[8]) const {
+    asm volatile("ds_read_b128 %0, %1 offset:%2"
+                 : "=v"(f[X])
+                 : "v"(fa), "i"(SLOT * 512 + X * 4096));
+  }
+};
+
+// Single-slice layout (with an MN-contiguous partner): slot s at s x 16 KB,
+// 256 rows of 64 bytes, 16-byte chunks XOR-swizzled by row; one load
+// instruction covers 16 rows x 64 bytes.
+template <>
+struct OpK<false> {
   const unsigned short *p;
   int64_t ld, row0, nrows, kbeg;
   unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
   int kc[4];         // their K offsets within the slice
-  unsigned fa;       // LDS address of this lane's fragment reads (block 0)
+  unsigned fa;       // LDS address of this lane's fragment reads (block 0, slot 0)
   __amdgpu_buffer_rsrc_t whole;  // the tile's rows from (row0, kbeg) to the end
 
   __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
@@ -158,35 +257,31 @@ struct OpK {
     fa = lds_base + unsigned(r * 64 + 16 * (c ^ swz_k(r)));
   }
   // Load chunk i of this thread's share of the slice starting at K = k0 into
-  // the stage at LDS byte offset `stage`. CHECK: the slice may end before
-  // k0 + BK, so chunks past kend are pointed outside the descriptor.
-  // Full slices (CHECK false) use one descriptor for the whole tile and
-  // step through K with the scalar offset: a row below nrows stays inside the
-  // descriptor at every k0 < K <= ld, and a row past it lies outside at every
-  // k0, whether or not the range check counts the scalar offset.
+  // slot `slot` (`ops`: the operand's LDS base). CHECK and the descriptor
+  // use are as for the paired layout.
   template <bool CHECK>
-  __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
-                                            int64_t kend) const {
+  __device__ __forceinline__ void issue_one(LDS_AS char *ops, int slot, int wave, int i,
+                                            int64_t k0, int64_t kend) const {
+    LDS_AS char *dst = ops + slot * kSliceBytes + (wave * 4 + i) * 1024;
     if constexpr (CHECK) {
       const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
       const unsigned v = k0 + kc[i] < kend ? voff[i] : kOOB;
-      load_lds16(r, stage + (wave * 4 + i) * 1024, v);
+      load_lds16(r, dst, v);
     } else {
-      load_lds16(whole, stage + (wave * 4 + i) * 1024, voff[i], unsigned(k0 - kbeg) * 2u);
+      load_lds16(whole, dst, voff[i], unsigned(k0 - kbeg) * 2u);
     }
   }
+  // (named by the paired pipeline's code, never called with this layout)
+  template <bool CHECK>
+  __device__ void issue_pair(LDS_AS char *, int, int, int, int64_t, int64_t) const {
+    static_assert(CHECK && !CHECK, "single-slice layout: load one slice at a time");
+  }
   static constexpr int kReads = 8;  // LDS reads per K-step
-  // Read X (0..7) of the K-step in the stage at LDS byte offset OFF: block X
-  // (rows wr + 16 X ..; adding 16 rows leaves the swizzle unchanged). The
-  // stage and block offsets are instruction immediates.
-  template <int OFF, int X>
+  template <int SLOT, int X>
   __device__ __forceinline__ void read(bf16x8 (&f)[8]) const {
-    // the read offset field is 16 bits: whole 64 KB steps go into the base
-    // (loop-invariant, so held in a register)
-    const unsigned base = fa + unsigned(OFF >> 16) * 65536u;
     asm volatile("ds_read_b128 %0, %1 offset:%2"
                  : "=v"(f[X])
-                 : "v"(base), "i"(OFF % 65536 + X * 1024));
+                 : "v"(fa), "i"(SLOT * kSliceBytes + X * 1024));
   }
 };
 
@@ -221,26 +316,36 @@ struct OpMN {
       fb[i] = lds_base + unsigned(k * 512 + 16 * (c ^ swz_mn(k)) + 8 * half);
     }
   }
-  // K-rows past kend lie outside the descriptor and read as zero, so no
-  // per-lane check is needed.
+  // Load chunk i (0..3) of the slice starting at K = k0 into slot `slot`.
   template <bool CHECK>
-  __device__ __forceinline__ void issue_one(LDS_AS char *stage, int wave, int i, int64_t k0,
-                                            int64_t kend) const {
+  __device__ __forceinline__ void issue_one(LDS_AS char *ops, int slot, int wave, int i,
+                                            int64_t k0, int64_t kend) const {
     const __amdgpu_buffer_rsrc_t r = rsrc(p + k0 * ld + col0, ((kend - k0) * ld - col0) * 2);
-    load_lds16(r, stage + (wave * 4 + i) * 1024, voff[i]);
+    load_lds16(r, ops + slot * kSliceBytes + (wave * 4 + i) * 1024, voff[i]);
+  }
+  // Load block i (0..7) of the pair of slices starting at K = k0 into the
+  // slots slot0, slot0 + 1 (`ops`: the operand's LDS base); each slot holds
+  // 32 K-rows of 512 bytes. K-rows past kend lie outside the descriptor and
+  // read as zero, so no per-lane check is needed.
+  template <bool CHECK>
+  __device__ __forceinline__ void issue_pair(LDS_AS char *ops, int slot0, int wave, int i,
+                                             int64_t k0, int64_t kend) const {
+    const int t = i >> 2;  // slice of the pair
+    const int64_t k = k0 + int64_t(t) * BK;
+    const __amdgpu_buffer_rsrc_t r = rsrc(p + k * ld + col0, ((kend - k) * ld - col0) * 2);
+    load_lds16(r, ops + (slot0 + t) * kSliceBytes + (wave * 4 + (i & 3)) * 1024, voff[i & 3]);
   }
   static constexpr int kReads = 16;  // LDS reads per K-step
-  // Read X (0..15) of the K-step in the stage at LDS byte offset OFF: block
-  // X / 2, K-values 4 (X % 2) .. + 3 of each lane's eight (the two halves of
-  // the MFMA operand).
-  template <int OFF, int X>
+  // Read X (0..15) of the K-step whose slice is in slot SLOT: block X / 2,
+  // K-values 4 (X % 2) .. + 3 of each lane's eight (the two halves of the
+  // MFMA operand).
+  template <int SLOT, int X>
   __device__ __forceinline__ void read(bf16x8 (&f)[8]) const {
     constexpr int i = X >> 1;
-    const unsigned base = fb[i] + unsigned(OFF >> 16) * 65536u;
     i16x4 v;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
                  : "=v"(v)
-                 : "v"(base), "i"(OFF % 65536 + (X & 1) * 4 * 512));
+                 : "v"(fb[i]), "i"(SLOT * kSliceBytes + (X & 1) * 4 * 512));
     auto w = __builtin_bit_cast(i16x8, f[i]);
     if constexpr (X & 1) {
       w = __builtin_shufflevector(w, __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1),
@@ -519,8 +624,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int wm = wave >> 1, wn = wave & 1;
   const unsigned lds_base = unsigned(reinterpret_cast<uintptr_t>(lds));
 
-  using OA = typename std::conditional<A_K, OpK, OpMN>::type;
-  using OB = typename std::conditional<B_K, OpK, OpMN>::type;
+  // Both operands K-contiguous (the logits GEMM): the paired pipeline.
+  constexpr bool PAIRED = A_K && B_K;
+  using OA = typename std::conditional<A_K, OpK<PAIRED>, OpMN>::type;
+  using OB = typename std::conditional<B_K, OpK<PAIRED>, OpMN>::type;
   OA opa;
   OB opb;
   if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, kbeg, wave, lane, wm * 128, lds_base);
@@ -528,6 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   if constexpr (B_K)
     opb.init(d.B, d.ldb, n0, d.N, kbeg, wave, lane, wn * 128, lds_base + kOperandBytes);
   else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128, lds_base + kOperandBytes);
+  LDS_AS char *lds_a = lds, *lds_b = lds + kOperandBytes;
 
   // acc[i][j]: the 16 x 16 block of rows wm * 128 + 16 i, columns wn * 128 + 16 j
   f32x4 acc[8][8];
@@ -552,17 +660,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     fb[0][i] = fb[1][i] = bf16x8{};
   }
   if (nkt > 0) {
-    // prologue: all NSTAGE stages in flight; wait for the first, read it
-    static_for<NSTAGE>([&](auto S) __attribute__((always_inline)) {
-      constexpr int s = decltype(S)::value;
-      const int64_t k0 = kbeg + int64_t(s) * BK;
+    // prologue: all NSTAGE slices in flight; wait for the first, read it
+    if constexpr (PAIRED) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        opa.template issue_one<true>(lds + s * kStageBytes, wave, q, k0, kend);
-        opb.template issue_one<true>(lds + s * kStageBytes + kOperandBytes, wave, q, k0, kend);
+      for (int pr = 0; pr < 2; ++pr) {
+        const int64_t k0 = kbeg + int64_t(2 * pr) * BK;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          opa.template issue_pair<true>(lds_a, 2 * pr, wave, q, k0, kend);
+          opb.template issue_pair<true>(lds_b, 2 * pr, wave, q, k0, kend);
+        }
       }
-    });
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntPrologue) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < NSTAGE; ++sl) {
+        const int64_t k0 = kbeg + int64_t(sl) * BK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          opa.template issue_one<true>(lds_a, sl, wave, q, k0, kend);
+          opb.template issue_one<true>(lds_b, sl, wave, q, k0, kend);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntPrologue) : "memory");
+    }
     __builtin_amdgcn_s_barrier();
     static_for<OA::kReads>([&](auto X) __attribute__((always_inline)) {
       opa.template read<0, decltype(X)::value>(fa[0]);
@@ -576,29 +697,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     constexpr int u = decltype(U_)::value;
     constexpr bool CHECK = decltype(CHECK_)::value;
     constexpr int cur = u & 1, nxt = cur ^ 1;
-    constexpr int s_nxt = ((u + 1) % NSTAGE) * kStageBytes;  // slice kt + 1
-    constexpr int s_cur = u * kStageBytes;                   // slice kt, free now
-    const int64_t k_load = kbeg + int64_t(kt + NSTAGE) * BK;
+    constexpr int slot_nxt = (u + 1) % NSTAGE;  // slice kt + 1
+    // Paired: odd steps load the pair kt + 3, kt + 4 into the slots of
+    // kt - 1 and kt, both free once every wave is past this step's barrier.
+    // Single: every step loads slice kt + NSTAGE into the slot of slice kt.
+    constexpr bool load_pair = PAIRED && (u & 1);
+    constexpr int slot_load = PAIRED ? (u + 3) % NSTAGE : u;
+    const int64_t k_load = kbeg + int64_t(kt + (PAIRED ? 3 : NSTAGE)) * BK;
     // Slice kt + 1 is in LDS for every wave, and every wave has its slice-kt
-    // fragments (so the stage of slice kt can be refilled): of this thread's
-    // loads only those of slices kt + 2 and kt + 3 may still be in flight.
+    // fragments. Of this thread's loads, those still allowed in flight are:
+    // paired, those of the pair after the one holding slice kt + 1 (none at
+    // odd steps, whose slice kt + 1 starts the most recently loaded pair);
+    // single, those of slices kt + 2 and kt + 3.
+    constexpr int vm = PAIRED ? (load_pair ? 0 : kLoadsPerPair) : kVmcntLoop;
     wait_lds();
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmcntLoop) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(vm) : "memory");
     __builtin_amdgcn_s_barrier();
-    // 64 MFMAs; between them the reads of slice kt + 1 and the 8 loads of
-    // slice kt + NSTAGE (4 of A, then 4 of B).
+    // 64 MFMAs; between them the reads of slice kt + 1 and the loads: paired,
+    // at odd steps, the 16 of the next pair (8 of A, then 8 of B); single, 8
+    // per step (4 of A, then 4 of B).
     constexpr int ea = 64 / OA::kReads, eb = 64 / OB::kReads;
     static_for<64>([&](auto X_) __attribute__((always_inline)) {
       constexpr int x = decltype(X_)::value;
       mfma(acc[x >> 3][x & 7], fb[cur][x & 7], fa[cur][x >> 3]);
-      if constexpr (x % ea == 0) opa.template read<s_nxt, x / ea>(fa[nxt]);
-      if constexpr (x % eb == eb / 2) opb.template read<s_nxt, x / eb>(fb[nxt]);
-      if constexpr ((x & 7) == 4) {
+      if constexpr (x % ea == 0) opa.template read<slot_nxt, x / ea>(fa[nxt]);
+      if constexpr (x % eb == eb / 2) opb.template read<slot_nxt, x / eb>(fb[nxt]);
+      if constexpr (load_pair && (x & 3) == 2) {
+        constexpr int q = x >> 2;
+        if constexpr (q < 8)
+          opa.template issue_pair<CHECK>(lds_a, slot_load, wave, q, k_load, kend);
+        else
+          opb.template issue_pair<CHECK>(lds_b, slot_load, wave, q - 8, k_load, kend);
+      }
+      if constexpr (!PAIRED && (x & 7) == 4) {
         constexpr int q = x >> 3;
         if constexpr (q < 4)
-          opa.template issue_one<CHECK>(lds + s_cur, wave, q, k_load, kend);
+          opa.template issue_one<CHECK>(lds_a, slot_load, wave, q, k_load, kend);
         else
-          opb.template issue_one<CHECK>(lds + s_cur + kOperandBytes, wave, q - 4, k_load, kend);
+          opb.template issue_one<CHECK>(lds_b, slot_load, wave, q - 4, k_load, kend);
       }
     });
   };
