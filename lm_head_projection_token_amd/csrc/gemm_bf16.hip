@@ -25,18 +25,19 @@
 // operand (128 KB of LDS) hold four K-slices. The buffer descriptors give
 // zero fill for rows past the end of an operand; K-chunks past the end are
 // pointed outside the descriptor's range and read as zero as well.
-//   K-contiguous operands, when both are (the logits GEMM), are loaded a
-//   pair of slices at a time: one load instruction covers 8 rows x 128
-//   contiguous bytes (two slices of the same 8 rows, whole cache lines), so
-//   the texture path handles half the rows per instruction that single
-//   slices (16 rows x 64 bytes, half lines) would need; in LDS the slices of
-//   a pair sit 512 bytes apart inside 2 KB blocks of 8 rows, 16-byte chunks
-//   XOR-swizzled by row, read with ds_read_b128. A pair is loaded during the
-//   odd K-step that frees its two slots, about one and a half K-steps before
-//   its first slice is read.
-//   With an MN-contiguous partner (dX, dW) each K-step loads the slice four
-//   steps ahead, about two and a half K-steps before it is read; the
-//   K-contiguous operand then keeps 256 rows of 64 bytes per slot.
+//   K-contiguous operands are loaded a pair of slices at a time: one load
+//   instruction covers 8 rows x 128 contiguous bytes (two slices of the same
+//   8 rows, whole cache lines), so the texture path handles half the rows
+//   per instruction that single slices (16 rows x 64 bytes, half lines)
+//   would need: measured 10 % off the logits GEMM and 4-5 % off dX. In LDS
+//   the slices of a pair sit 512 bytes apart inside 2 KB blocks of 8 rows,
+//   16-byte chunks XOR-swizzled by row, read with ds_read_b128. A pair is
+//   loaded during the odd K-step that frees its two slots, about one and a
+//   half K-steps before its first slice is read.
+//   MN-contiguous operands (B of dX, both of dW) load one slice per K-step,
+//   four steps ahead (about two and a half K-steps before it is read): a
+//   shorter lead cost dX and dW 1-2 %, and their loads already cover whole
+//   lines.
 //   MN-contiguous operands keep their memory layout: 32 K-rows of 512 bytes
 //   per slot (each load already covers whole lines), chunks XOR-swizzled by
 //   K-row, read with ds_read_b64_tr_b16, whose 16-lane transpose hands each
@@ -150,11 +151,7 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, LDS_AS void
 // XOR-swizzled by row. One load instruction covers one block of both slices
 // of a pair: lanes 0-31 the first slice, lanes 32-63 the second, i.e. 8 rows
 // x 128 contiguous bytes of global memory, whole cache lines.
-template <bool PAIRED>
-struct OpK;
-
-template <>
-struct OpK<true> {
+struct OpK {
   const unsigned short *p;
   int64_t ld, row0, nrows, kbeg;
   unsigned voff[8];  // byte offsets of this thread's 8 pair chunks from (row0, k0)
@@ -206,10 +203,10 @@ struct OpK<true> {
       load_lds16(whole, dst, voff[i], unsigned(k0 - kbeg) * 2u);
     }
   }
-  // (named by the single pipeline's code, never called with this layout)
+  // (named by the code for MN-contiguous operands, never called here)
   template <bool CHECK>
   __device__ void issue_one(LDS_AS char *, int, int, int, int64_t, int64_t) const {
-    static_assert(CHECK && !CHECK, "paired layout: load pairs of slices");
+    static_assert(CHECK && !CHECK, "K-contiguous operands load pairs of slices");
   }
   static constexpr int kReads = 8;  // LDS reads per K-step
   // Read X (0..7) of the K-step whose slice is in slot SLOT: block X (rows
@@ -220,68 +217,6 @@ struct OpK<true> {
     asm volatile("ds_read_b128 %0, %1 offset:%2"
                  : "=v"(f[X])
                  : "v"(fa), "i"(SLOT * 512 + X * 4096));
-  }
-};
-
-// Single-slice layout (with an MN-contiguous partner): slot s at s x 16 KB,
-// 256 rows of 64 bytes, 16-byte chunks XOR-swizzled by row; one load
-// instruction covers 16 rows x 64 bytes.
-template <>
-struct OpK<false> {
-  const unsigned short *p;
-  int64_t ld, row0, nrows, kbeg;
-  unsigned voff[4];  // byte offsets of this thread's 4 chunks from (row0, k0)
-  int kc[4];         // their K offsets within the slice
-  unsigned fa;       // LDS address of this lane's fragment reads (block 0, slot 0)
-  __amdgpu_buffer_rsrc_t whole;  // the tile's rows from (row0, kbeg) to the end
-
-  __device__ __forceinline__ void init(const unsigned short *p_, int64_t ld_, int64_t row0_,
-                                       int64_t nrows_, int64_t kbeg_, int wave, int lane,
-                                       int wr, unsigned lds_base) {
-    p = p_;
-    ld = ld_;
-    row0 = row0_;
-    nrows = nrows_;
-    kbeg = kbeg_;
-    whole = rsrc(p + row0 * ld + kbeg, ((nrows - row0) * ld - kbeg) * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (wave * 4 + i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz_k(r);
-      voff[i] = unsigned((int64_t(r) * ld + 8 * c) * 2);
-      kc[i] = 8 * c;
-    }
-    // lane l: row l % 16 of each 16-row block, K-values 8 (l / 16) .. + 7
-    const int r = wr + (lane & 15);
-    const int c = lane >> 4;
-    fa = lds_base + unsigned(r * 64 + 16 * (c ^ swz_k(r)));
-  }
-  // Load chunk i of this thread's share of the slice starting at K = k0 into
-  // slot `slot` (`ops`: the operand's LDS base). CHECK and the descriptor
-  // use are as for the paired layout.
-  template <bool CHECK>
-  __device__ __forceinline__ void issue_one(LDS_AS char *ops, int slot, int wave, int i,
-                                            int64_t k0, int64_t kend) const {
-    LDS_AS char *dst = ops + slot * kSliceBytes + (wave * 4 + i) * 1024;
-    if constexpr (CHECK) {
-      const __amdgpu_buffer_rsrc_t r = rsrc(p + row0 * ld + k0, ((nrows - row0) * ld - k0) * 2);
-      const unsigned v = k0 + kc[i] < kend ? voff[i] : kOOB;
-      load_lds16(r, dst, v);
-    } else {
-      load_lds16(whole, dst, voff[i], unsigned(k0 - kbeg) * 2u);
-    }
-  }
-  // (named by the paired pipeline's code, never called with this layout)
-  template <bool CHECK>
-  __device__ void issue_pair(LDS_AS char *, int, int, int, int64_t, int64_t) const {
-    static_assert(CHECK && !CHECK, "single-slice layout: load one slice at a time");
-  }
-  static constexpr int kReads = 8;  // LDS reads per K-step
-  template <int SLOT, int X>
-  __device__ __forceinline__ void read(bf16x8 (&f)[8]) const {
-    asm volatile("ds_read_b128 %0, %1 offset:%2"
-                 : "=v"(f[X])
-                 : "v"(fa), "i"(SLOT * kSliceBytes + X * 1024));
   }
 };
 
@@ -624,10 +559,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int wm = wave >> 1, wn = wave & 1;
   const unsigned lds_base = unsigned(reinterpret_cast<uintptr_t>(lds));
 
-  // Both operands K-contiguous (the logits GEMM): the paired pipeline.
+  // K-contiguous operands load pairs of slices, MN-contiguous ones single
+  // slices: both paired (logits), A paired and B single (dX), both single (dW).
   constexpr bool PAIRED = A_K && B_K;
-  using OA = typename std::conditional<A_K, OpK<PAIRED>, OpMN>::type;
-  using OB = typename std::conditional<B_K, OpK<PAIRED>, OpMN>::type;
+  constexpr bool HYBRID = A_K && !B_K;
+  using OA = typename std::conditional<A_K, OpK, OpMN>::type;
+  using OB = typename std::conditional<B_K, OpK, OpMN>::type;
   OA opa;
   OB opb;
   if constexpr (A_K) opa.init(d.A, d.lda, m0, d.M, kbeg, wave, lane, wm * 128, lds_base);
@@ -672,6 +609,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
         }
       }
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
+    } else if constexpr (HYBRID) {
+      // in the order the steady state issues them: B 0, B 1, A (0, 1),
+      // B 2, B 3, A (2, 3); slice 0 of both needs all but the last 16
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int sl = 2 * pr + t;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            opb.template issue_one<true>(lds_b, sl, wave, q, kbeg + int64_t(sl) * BK, kend);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          opa.template issue_pair<true>(lds_a, 2 * pr, wave, q, kbeg + int64_t(2 * pr) * BK, kend);
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
     } else {
 #pragma unroll
       for (int sl = 0; sl < NSTAGE; ++sl) {
@@ -701,15 +655,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     // Paired: odd steps load the pair kt + 3, kt + 4 into the slots of
     // kt - 1 and kt, both free once every wave is past this step's barrier.
     // Single: every step loads slice kt + NSTAGE into the slot of slice kt.
+    // Hybrid: every step loads B's slice kt + NSTAGE into the slot of slice
+    // kt, odd steps then A's pair kt + 3, kt + 4.
     constexpr bool load_pair = PAIRED && (u & 1);
     constexpr int slot_load = PAIRED ? (u + 3) % NSTAGE : u;
     const int64_t k_load = kbeg + int64_t(kt + (PAIRED ? 3 : NSTAGE)) * BK;
+    constexpr int slot_pair = (u + 3) % NSTAGE;
+    const int64_t k_pair = kbeg + int64_t(kt + 3) * BK;
     // Slice kt + 1 is in LDS for every wave, and every wave has its slice-kt
     // fragments. Of this thread's loads, those still allowed in flight are:
     // paired, those of the pair after the one holding slice kt + 1 (none at
     // odd steps, whose slice kt + 1 starts the most recently loaded pair);
     // single, those of slices kt + 2 and kt + 3.
-    constexpr int vm = PAIRED ? (load_pair ? 0 : kLoadsPerPair) : kVmcntLoop;
+    // hybrid: at even steps B's slices kt + 2, kt + 3 and A's pair after the
+    // one holding slice kt + 1 (16); at odd steps only the B slice loaded
+    // by the step before (4), since A's pair holding slice kt + 1 was the
+    // last thing issued before it.
+    constexpr int vm = PAIRED   ? (load_pair ? 0 : kLoadsPerPair)
+                       : HYBRID ? ((u & 1) ? 4 : kLoadsPerPair)
+                                : kVmcntLoop;
     wait_lds();
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(vm) : "memory");
     __builtin_amdgcn_s_barrier();
@@ -729,7 +693,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
         else
           opb.template issue_pair<CHECK>(lds_b, slot_load, wave, q - 8, k_load, kend);
       }
-      if constexpr (!PAIRED && (x & 7) == 4) {
+      if constexpr (HYBRID && (u & 1) && (x & 3) == 2) {
+        constexpr int q = x >> 2;  // B's 4 loads first, then A's 8 pair loads
+        if constexpr (q < 4)
+          opb.template issue_one<CHECK>(lds_b, slot_load, wave, q, k_load, kend);
+        else if constexpr (q < 12)
+          opa.template issue_pair<CHECK>(lds_a, slot_pair, wave, q - 4, k_pair, kend);
+      }
+      if constexpr (HYBRID && !(u & 1) && (x & 15) == 4)
+        opb.template issue_one<CHECK>(lds_b, slot_load, wave, x >> 4, k_load, kend);
+      if constexpr (!PAIRED && !HYBRID && (x & 7) == 4) {
         constexpr int q = x >> 3;
         if constexpr (q < 4)
           opa.template issue_one<CHECK>(lds_a, slot_load, wave, q, k_load, kend);
