@@ -75,6 +75,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 #ifndef FLL_GEMM_STAGES
@@ -341,15 +342,19 @@ struct EpiLogits {
   __device__ __forceinline__ float col_bias(int64_t n) const {
     return bias ? __uint_as_float(unsigned(bias[n]) << 16) : 0.0f;
   }
-  // store4_in: the four columns are inside the matrix
+  // store4_in: the four columns are inside the matrix. Non-temporal: the
+  // chunk's logits (GBs) are read once, by the row kernel, after the whole
+  // GEMM; streaming them past the caches measured 2.5 % off the GEMM and 3 %
+  // off the row kernel.
   __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int) const {
     if constexpr (B16) {
-      uint2 pk;
+      u32x2 pk;
       pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
       pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
-      *reinterpret_cast<uint2 *>(static_cast<unsigned short *>(S) + m * lds + n) = pk;
+      __builtin_nontemporal_store(
+          pk, reinterpret_cast<u32x2 *>(static_cast<unsigned short *>(S) + m * lds + n));
     } else {
-      *reinterpret_cast<f32x4 *>(static_cast<float *>(S) + m * lds + n) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(static_cast<float *>(S) + m * lds + n));
     }
   }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, int64_t nmax, float4 v,

@@ -304,7 +304,8 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     coef = (HEAD == HEAD_CE ? -g : g) * w * a.inv_tau;
   }
 
-  // ---- dZ = dS / tau, written in place ----
+  // ---- dZ = dS / tau, written in place (bf16 with non-temporal stores: the
+  // next reader is the dX GEMM, after the whole chunk) ----
   // The bf16 dZ of element v goes to bytes [2v, 2v + 2) of the row. Over
   // fp32 logits those are float slots that an earlier strip (or this strip,
   // before the barrier) has already read; each strip's loads complete before
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
           uint2 pk;
           pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
           pk.y = (unsigned)f2bf(d[2]) | ((unsigned)f2bf(d[3]) << 16);
-          *reinterpret_cast<uint2 *>(Zb + e) = pk;
+          __builtin_nontemporal_store(u32x2_t{pk.x, pk.y}, reinterpret_cast<u32x2_t *>(Zb + e));
         } else {
           for (int i = 0; i < 4; ++i)
             if (e + i < V) Zb[e + i] = f2bf(d[i]);
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
           uint2 pk;
           pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
           pk.y = (unsigned)f2bf(d[2]) | ((unsigned)f2bf(d[3]) << 16);
-          *reinterpret_cast<uint2 *>(Zb + e) = pk;
+          __builtin_nontemporal_store(u32x2_t{pk.x, pk.y}, reinterpret_cast<u32x2_t *>(Zb + e));
         } else {
           for (int i = 0; i < 4; ++i)
             if (e + i < V) Zb[e + i] = f2bf(d[i]);
