@@ -433,7 +433,8 @@ struct EpiDx {
 };
 
 // dW epilogue: fp32 store, or read-modify-write across token chunks (each
-// tile owns its rows, so there are no atomics).
+// tile owns its rows, so there are no atomics). The interior tiles' loads and
+// stores are non-temporal: dW (GBs) is touched once per chunk.
 struct EpiDw {
   static constexpr bool kRowStats = false;
   static constexpr bool kReadModifyWrite = true;
@@ -442,10 +443,10 @@ struct EpiDw {
   int accumulate;
   __device__ __forceinline__ f32x4 load4_in(int64_t m, int64_t n) const {
     if (!accumulate) return f32x4{0.f, 0.f, 0.f, 0.f};
-    return *reinterpret_cast<const f32x4 *>(dW + m * ld + n);
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(dW + m * ld + n));
   }
   __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int) const {
-    *reinterpret_cast<f32x4 *>(dW + m * ld + n) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dW + m * ld + n));
   }
   __device__ __forceinline__ float4 load4(int64_t m, int64_t n, int64_t nmax) const {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
