@@ -84,11 +84,13 @@ def row_bytes_per_valid_row(case, logits_bf16=False):
     return (s + extra + 2) * case.V
 
 
-def sample_clock(step, sync, samples=3):
-    """Average shader clock (GHz) while steps run back to back: `amd-smi
-    metric --clock` is read a few times from a helper thread, each reading
-    averaged over the GFX clock of every XCD. None if amd-smi is missing or
-    prints no GFX clock."""
+def sample_clock(step, sync, samples=6):
+    """Shader clock (GHz) while steps run back to back: `amd-smi metric
+    --clock` is read a few times from a helper thread, each reading averaged
+    over the GFX clock of every XCD. Returns (mean, min, max) of the
+    readings and their count, or None if amd-smi is missing or prints no GFX clock. Each
+    reading is instantaneous, so the mean mixes GEMM and row-kernel phases;
+    the per-kernel clocks come from the counters (GRBM_COUNT)."""
     import re
     import shutil
     import subprocess
@@ -122,7 +124,10 @@ def sample_clock(step, sync, samples=3):
             step()
         sync()
     th.join(timeout=30)
-    return sum(readings) / len(readings) / 1e3 if readings else None
+    if not readings:
+        return None
+    return (sum(readings) / len(readings) / 1e3, min(readings) / 1e3, max(readings) / 1e3,
+            len(readings))
 
 
 def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
@@ -316,14 +321,16 @@ def main():
         # The chip's power limit sets the shader clock under this load; the
         # dense peak above assumes 2.4 GHz. Reported beside it, not instead.
         print("[bench] reading the shader clock while steps run", file=sys.stderr, flush=True)
-        ghz = sample_clock(step, torch.cuda.synchronize)
-        if ghz:
+        clk = sample_clock(step, torch.cuda.synchronize)
+        if clk:
+            ghz = clk[0]
             peak_at_clock = PEAK_BF16_TFLOPS * ghz / 2.4 if case.dtype == "bf16" else \
                 PEAK_FP32_TFLOPS * ghz / 2.4
             out["clock"] = {
                 "source": "amd-smi metric --clock (GFX clock averaged over the XCDs) while "
                           "steps ran back to back after the timed region",
-                "GHz": ghz, "peak_at_clock": peak_at_clock,
+                "GHz": ghz, "GHz_min": clk[1], "GHz_max": clk[2], "readings": clk[3],
+                "peak_at_clock": peak_at_clock,
                 "end_to_end_frac_at_clock": gemm_flops(case) / (ms / 1e3) / 1e12 / peak_at_clock,
                 "roofline_frac_at_clock": achieved / peak_at_clock}
     if not args.no_cpu_baseline:
