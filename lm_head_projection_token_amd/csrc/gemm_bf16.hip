@@ -319,11 +319,15 @@ struct GemmDesc {
 // Logits epilogue: S = (acc + b[n]) * inv_tau, fp32, plus the row statistics
 // of each 128-column half-tile: max and sum of exp(S - max) over its columns
 // below N, written as stats[m * n_stat + n / 128] (when stats is given).
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction per pair; a NaN stays a NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ unsigned short f2bf(float f) {
-  unsigned int u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  return (unsigned short)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // Logits epilogue: S row-major, pitch lds elements, fp32 or (B16) bf16
@@ -349,8 +353,8 @@ struct EpiLogits {
   __device__ __forceinline__ void store4_in(int64_t m, int64_t n, f32x4 v, int) const {
     if constexpr (B16) {
       u32x2 pk;
-      pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
-      pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+      pk.x = pack_bf16x2(v.x, v.y);
+      pk.y = pack_bf16x2(v.z, v.w);
       __builtin_nontemporal_store(
           pk, reinterpret_cast<u32x2 *>(static_cast<unsigned short *>(S) + m * lds + n));
     } else {
@@ -364,8 +368,8 @@ struct EpiLogits {
       unsigned short *p = static_cast<unsigned short *>(S) + m * lds + n;
       if (n + 4 <= nmax) {
         uint2 pk;
-        pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
-        pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+        pk.x = pack_bf16x2(v.x, v.y);
+        pk.y = pack_bf16x2(v.z, v.w);
         *reinterpret_cast<uint2 *>(p) = pk;
       } else {
 #pragma unroll
@@ -399,8 +403,8 @@ struct EpiDx {
       *reinterpret_cast<f32x4 *>(partial + (int64_t(split) * M + m) * N + n) = v;
     } else {
       uint2 pk;
-      pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
-      pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+      pk.x = pack_bf16x2(v.x, v.y);
+      pk.y = pack_bf16x2(v.z, v.w);
       *reinterpret_cast<uint2 *>(out + m * ldo + n) = pk;
     }
   }
@@ -420,8 +424,8 @@ struct EpiDx {
       unsigned short *p = out + m * ldo + n;
       if (n + 4 <= nmax) {
         uint2 pk;
-        pk.x = unsigned(f2bf(v.x)) | (unsigned(f2bf(v.y)) << 16);
-        pk.y = unsigned(f2bf(v.z)) | (unsigned(f2bf(v.w)) << 16);
+        pk.x = pack_bf16x2(v.x, v.y);
+        pk.y = pack_bf16x2(v.z, v.w);
         *reinterpret_cast<uint2 *>(p) = pk;
       } else {
 #pragma unroll

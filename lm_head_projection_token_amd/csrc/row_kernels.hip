@@ -48,12 +48,15 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
   m = mn;
 }
 
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction per pair; a NaN stays a NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ unsigned short f2bf(float f) {
-  // round to nearest even; quiet NaN stays NaN
-  unsigned int u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  return (unsigned short)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // bf16 dZ rows are read by the GEMMs in 8-element chunks; the slots from V to
@@ -343,8 +346,8 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
       if (SB || a.dz_bf16) {
         if (e + 4 <= V) {
           uint2 pk;
-          pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
-          pk.y = (unsigned)f2bf(d[2]) | ((unsigned)f2bf(d[3]) << 16);
+          pk.x = pack_bf16x2(d[0], d[1]);
+          pk.y = pack_bf16x2(d[2], d[3]);
           __builtin_nontemporal_store(u32x2_t{pk.x, pk.y}, reinterpret_cast<u32x2_t *>(Zb + e));
         } else {
           for (int i = 0; i < 4; ++i)
@@ -545,8 +548,8 @@ __global__ __launch_bounds__(kRowThreads) void jsd_row_kernel(RowArgs a) {
       if (SB || a.dz_bf16) {
         if (e + 4 <= V) {
           uint2 pk;
-          pk.x = (unsigned)f2bf(d[0]) | ((unsigned)f2bf(d[1]) << 16);
-          pk.y = (unsigned)f2bf(d[2]) | ((unsigned)f2bf(d[3]) << 16);
+          pk.x = pack_bf16x2(d[0], d[1]);
+          pk.y = pack_bf16x2(d[2], d[3]);
           __builtin_nontemporal_store(u32x2_t{pk.x, pk.y}, reinterpret_cast<u32x2_t *>(Zb + e));
         } else {
           for (int i = 0; i < 4; ++i)
@@ -699,8 +702,8 @@ __global__ void dx_reduce_kernel(const float *P, int64_t splits, int64_t M, int6
   }
   if (out_bf16) {
     uint2 pk;
-    pk.x = (unsigned)f2bf(acc.x) | ((unsigned)f2bf(acc.y) << 16);
-    pk.y = (unsigned)f2bf(acc.z) | ((unsigned)f2bf(acc.w) << 16);
+    pk.x = pack_bf16x2(acc.x, acc.y);
+    pk.y = pack_bf16x2(acc.z, acc.w);
     *reinterpret_cast<uint2 *>(static_cast<unsigned short *>(dX) + m * ldo + c) = pk;
   } else {
     *reinterpret_cast<float4 *>(static_cast<float *>(dX) + m * ldo + c) = acc;
