@@ -478,8 +478,8 @@ struct EpiDw {
 
 // The inner loop's MFMAs and LDS fragment reads are volatile inline assembly,
 // so they issue in exactly the order written: each K-step interleaves the
-// reads of the next K-step's fragments and the loads of a new stage with
-// its 64 MFMAs. The compiler neither sees the reads' latency nor
+// reads of the next K-step's fragments and its share of the slice loads
+// with its 64 MFMAs. The compiler neither sees the reads' latency nor
 // treats the asm as MFMAs, so the LDS waits are explicit and the accumulators
 // rest a few cycles before the epilogue reads them.
 __device__ __forceinline__ void mfma(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
@@ -593,10 +593,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 
   // K-step kt (the last one may be partial) multiplies the fragments of
   // slice kt, held in registers; meanwhile it reads the fragments of slice
-  // kt + 1 from its stage into the other register set and loads slice
-  // kt + NSTAGE into the stage slice kt occupied. The loop is unrolled by
-  // NSTAGE (even), so every stage offset and register set below is a
-  // compile-time constant.
+  // kt + 1 from its slot into the other register set and issues loads into
+  // slots already consumed (see the staging note at the top). The loop is
+  // unrolled by NSTAGE (even), so every slot offset and register set below
+  // is a compile-time constant.
   const int nkt = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
   const int nkt_full = kend > kbeg ? int((kend - kbeg) / BK) : 0;
 
