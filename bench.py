@@ -84,10 +84,11 @@ def row_bytes_per_valid_row(case, logits_bf16=False):
     return (s + extra + 2) * case.V
 
 
-def sample_clock(step, sync, samples=6):
+def sample_clock(step, sync, ms_per_step, samples=6):
     """Shader clock (GHz) while steps run back to back: `amd-smi metric
     --clock` is read a few times from a helper thread, each reading averaged
-    over the GFX clock of every XCD. Returns (mean, min, max) of the
+    over the GFX clock of every XCD. Steps are queued ~100 ms at a time so
+    that the GPU does not idle between them while a reading is taken. Returns (mean, min, max) of the
     readings and their count, or None if amd-smi is missing or prints no GFX clock. Each
     reading is instantaneous, so the mean mixes GEMM and row-kernel phases;
     the per-kernel clocks come from the counters (GRBM_COUNT)."""
@@ -119,8 +120,9 @@ def sample_clock(step, sync, samples=6):
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
     t_end = time.perf_counter() + 60.0
+    batch = max(10, int(100.0 / max(ms_per_step, 1e-3)))
     while not done.is_set() and time.perf_counter() < t_end:
-        for _ in range(10):
+        for _ in range(batch):
             step()
         sync()
     th.join(timeout=30)
@@ -321,7 +323,7 @@ def main():
         # The chip's power limit sets the shader clock under this load; the
         # dense peak above assumes 2.4 GHz. Reported beside it, not instead.
         print("[bench] reading the shader clock while steps run", file=sys.stderr, flush=True)
-        clk = sample_clock(step, torch.cuda.synchronize)
+        clk = sample_clock(step, torch.cuda.synchronize, ms)
         if clk:
             ghz = clk[0]
             peak_at_clock = PEAK_BF16_TFLOPS * ghz / 2.4 if case.dtype == "bf16" else \
