@@ -1,6 +1,8 @@
-"""Host-side tools, without a GPU: bench.py's one-GPU guard and its flop /
-byte bookkeeping, the rocprofv3 summaries of the profiling module on small
-synthetic CSV files, and the build entry point on a fresh checkout.
+"""Host-side tools: bench.py's one-GPU guard, its flop / byte bookkeeping
+and its CPU-oracle timing, the rocprofv3 summaries of the profiling module
+on small synthetic CSV files, and the build entry point on a fresh checkout
+(all without a GPU); and, marked gpu, bench.py's JSON line on a small
+workload.
 """
 
 import csv
@@ -161,3 +163,38 @@ def test_build_module_loads_without_the_package():
     assert res.returncode == 0, res.stderr
     entry = open(os.path.join(ROOT, "__graft_entry__.py")).read()
     assert "spec_from_file_location" in entry
+
+
+def test_cpu_baseline_reports_the_oracle_on_a_row_sample():
+    case = workloads.small_case(BT=64, H=32, V=100, head="selective", reduction="mean",
+                                ignore_frac=0.1, seed=7)
+    inp = workloads.make_inputs(case)
+    out = bench.cpu_baseline(inp, case, rows_small=8, rows_big=32)
+    assert out["kind"] == "oracle" and out["unit"] == "tokens/s"
+    assert out["value"] > 0 and out["cores"] >= 1
+    assert "extrapolated linearly to BT=64" in out["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_json_line_on_the_gpu():
+    """The benchmark's one JSON line: the fields the contract names, the
+    roofline of the dominant GEMM and the per-kernel times (the V=32000 KL
+    workload, a few steps)."""
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "2",
+                          "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-clock"],
+                         capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [l for l in res.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] == pytest.approx(1024 / (d["ms_per_step"] / 1e3), rel=1e-6)
+    r = d["roofline"]
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    assert 0.0 < r["frac"] < 1.0
+    assert {"logits", "row", "dx", "prep", "final"} <= set(d["kernels"])
