@@ -328,6 +328,10 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
                         : nullptr;
   const bool bf16 = p.dtype == FLL_BF16;
   const size_t esz = bf16 ? 2 : 4;
+  // bf16 chunk logits: the label heads take the label's logit in fp32 from
+  // the logits GEMM, through the per-row buffer the row kernel then fills
+  const bool label_head = p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY;
+  float *label_logit = bf16 && p.logits_bf16 && label_head && a.labels ? rowval : nullptr;
   const float inv_tau = 1.0f / p.temperature;
 
   if (p.BT == 0) {
@@ -357,7 +361,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       if (bf16)
         fll::launch_logits_bf16(Xtc, p.H_teacher, a.W_teacher, p.H_teacher, a.b_teacher,
                                 inv_tau, T, plan->s_pitch, p.logits_bf16, stats_t,
-                                plan->stat_tiles, rows, p.V, p.H_teacher, s);
+                                plan->stat_tiles, rows, p.V, p.H_teacher, nullptr, 0,
+                                nullptr, s);
       else
         fll::launch_logits_f32(reinterpret_cast<const float *>(Xtc), p.H_teacher,
                                static_cast<const float *>(a.W_teacher), p.H_teacher,
@@ -369,7 +374,8 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       Probe pr(FLL_K_LOGITS, s);
       if (bf16)
         fll::launch_logits_bf16(Xc, p.H, a.W, p.H, a.b, inv_tau, S, plan->s_pitch,
-                                p.logits_bf16, stats, plan->stat_tiles, rows, p.V, p.H, s);
+                                p.logits_bf16, stats, plan->stat_tiles, rows, p.V, p.H,
+                                a.labels, r0, label_logit, s);
       else
         fll::launch_logits_f32(reinterpret_cast<const float *>(Xc), p.H,
                                static_cast<const float *>(a.W), p.H,
@@ -399,6 +405,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       ra.n_stat = plan->stat_tiles;
       ra.T = T;
       ra.stats_t = stats_t;
+      ra.label_logit = label_logit;
       Probe pr(FLL_K_ROW, s);
       fll::launch_row(ra, s);
     }

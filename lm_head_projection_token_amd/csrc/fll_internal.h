@@ -22,9 +22,14 @@ struct DevScalars {
 // If stats != nullptr, also writes for every row m and 128-column block t
 // the block's max and sum of exp(S - max) of the fp32 values:
 // stats[m * n_stat + t] = (max, sum), n_stat = ceil(N / 128).
+// label_logit (or null): for each row m with a label y = labels[label_row0
+// + m] inside [0, N), the fp32 logit S[m, y] is written to
+// label_logit[label_row0 + m] (bf16 chunk logits keep the label's logit
+// exact for the selective and cross-entropy heads).
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
                         const void *b, float inv_tau, void *S, int64_t lds, int s_bf16,
                         float2 *stats, int64_t n_stat, int64_t M, int64_t N, int64_t K,
+                        const int64_t *labels, int64_t label_row0, float *label_logit,
                         hipStream_t st);
 
 // dX = dZ W. dZ: bf16 [M x K] row pitch ldz (elements); W: [K x N] pitch ldw.
@@ -90,6 +95,7 @@ struct RowArgs {
   int64_t n_stat;         // blocks per row
   const float *T;         // JSD: the chunk's teacher logits (pitch s_pitch) or null
   const float2 *stats_t;  // JSD: the teacher's block statistics or null
+  const float *label_logit;  // global [BT]: fp32 S[r, y_r] from the logits GEMM, or null
 };
 void launch_row(const RowArgs &a, hipStream_t st);
 

@@ -103,7 +103,7 @@ constexpr int kVmcntPrologue = kLoadsPerSlice * (NSTAGE - 1);
 // Epilogue slab: 16 rows of the wave's 128 fp32 columns, rows 528 bytes apart.
 constexpr int kSlabPitch = 132;                     // floats
 constexpr int kSlabBytes = 16 * kSlabPitch * 4;     // 8448 per wave
-static_assert(4 * kSlabBytes + BN * 4 <= NSTAGE * kStageBytes,
+static_assert(4 * kSlabBytes + BN * 4 + BM * 4 <= NSTAGE * kStageBytes,
               "epilogue slabs and bias table reuse the stages");
 constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
 constexpr unsigned kMaxRecords = 0x7fffffffu;
@@ -343,6 +343,9 @@ struct EpiLogits {
   float inv_tau;
   float2 *stats;
   int64_t n_stat;
+  const int64_t *labels;  // label_logit: see launch_logits_bf16
+  int64_t label_row0;
+  float *label_logit;
   __device__ __forceinline__ float col_bias(int64_t n) const {
     return bias ? __uint_as_float(unsigned(bias[n]) << 16) : 0.0f;
   }
@@ -755,11 +758,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   // waves' slabs: read per slab, it is not held in registers across the
   // epilogue.
   LDS_AS float *btab = (LDS_AS float *)(lds + 4 * kSlabBytes);
+  // and the labels of the tile's 256 rows when the label logits are asked
+  // for (-1: no label in [0, N))
+  LDS_AS int *ltab = (LDS_AS int *)(lds + 4 * kSlabBytes + BN * 4);
   if constexpr (Epi::kRowStats) {
-    if (epi.bias) {
-      btab[t] = n0 + t < d.N ? epi.col_bias(n0 + t) : 0.0f;
-      __syncthreads();
+    if (epi.bias) btab[t] = n0 + t < d.N ? epi.col_bias(n0 + t) : 0.0f;
+    if (epi.label_logit) {
+      const int64_t y = m0 + t < d.M ? epi.labels[epi.label_row0 + m0 + t] : -1;
+      ltab[t] = y >= 0 && y < d.N ? int(y) : -1;
     }
+    if (epi.bias || epi.label_logit) __syncthreads();
   }
   LDS_AS float *slab = (LDS_AS float *)(lds + wave * kSlabBytes);
   const int lrow = lane & 15;
@@ -876,6 +884,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *(LDS_AS f32x4 *)(slab + lrow * kSlabPitch + 16 * j + lcol) = v[j];
+    if constexpr (Epi::kRowStats) {
+      // the label's fp32 logit, if it lies in this wave's 128 columns: one
+      // lane per row of the slab reads it back from the slab
+      if (epi.label_logit && lane < 16) {
+        const int off = ltab[wm * 128 + i * 16 + lane] - int(nw);
+        if (off >= 0 && off < 128)
+          epi.label_logit[epi.label_row0 + mw + i * 16 + lane] = slab[lane * kSlabPitch + off];
+      }
+    }
     // A wave's LDS operations complete in order, so the reads see the writes;
     // all eight are issued before the first store waits for them.
     f32x4 rd[8];
@@ -928,6 +945,7 @@ void launch(const GemmDesc &d0, const Epi &epi, hipStream_t st) {
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
                         const void *b, float inv_tau, void *S, int64_t lds, int s_bf16,
                         float2 *stats, int64_t n_stat, int64_t M, int64_t N, int64_t K,
+                        const int64_t *labels, int64_t label_row0, float *label_logit,
                         hipStream_t st) {
   GemmDesc d{};
   d.A = static_cast<const unsigned short *>(X);
@@ -943,10 +961,15 @@ void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
   d.n_first = 0;
   d.xcd_remap = 1;
   const auto *bias = static_cast<const unsigned short *>(b);
+  if (!labels) label_logit = nullptr;
   if (s_bf16)
-    launch<true, true>(d, EpiLogits<true>{S, lds, bias, inv_tau, stats, n_stat}, st);
+    launch<true, true>(d, EpiLogits<true>{S, lds, bias, inv_tau, stats, n_stat, labels,
+                                          label_row0, label_logit},
+                       st);
   else
-    launch<true, true>(d, EpiLogits<false>{S, lds, bias, inv_tau, stats, n_stat}, st);
+    launch<true, true>(d, EpiLogits<false>{S, lds, bias, inv_tau, stats, n_stat, labels,
+                                           label_row0, label_logit},
+                       st);
 }
 
 void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw, void *dX,

@@ -254,7 +254,10 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     }
   }
   float s_label = 0.0f;
-  if (HEAD != HEAD_KL && tid == 0) s_label = sr.at(y);  // read before any write
+  // read before any write; with bf16 chunk logits the logits GEMM left the
+  // fp32 logit of the label in label_logit (the per-row buffer this kernel
+  // overwrites at the end)
+  if (HEAD != HEAD_KL && tid == 0) s_label = a.label_logit ? a.label_logit[gr] : sr.at(y);
 
   // wave reduction, then across waves in a fixed order
   {

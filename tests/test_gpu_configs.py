@@ -75,7 +75,9 @@ def test_full_config_sampled(cfg):
     per = out["per_row"].cpu().double().numpy()
     scale = float(np.abs(ref["per_row"]).max())
     atol = 2e-3 * scale
-    if logits_bf16:  # plus what rounding the logits to bf16 can move a row's term
+    # plus what rounding the logits to bf16 can move a row's term; the label
+    # heads take the label's logit in fp32 from the GEMM, so theirs do not move
+    if logits_bf16 and case.head not in ("selective", "ce"):
         atol = atol + H.logit_rounding_bound(inp, case, rows)
     err = np.abs(per[rows.numpy()] - ref["per_row"])
     assert (err <= atol + 2e-3 * np.abs(ref["per_row"])).all(), \
