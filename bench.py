@@ -132,6 +132,27 @@ def sample_clock(step, sync, ms_per_step, samples=6):
             len(readings))
 
 
+def clock_record(clk, case, ms, achieved):
+    """The clock object of the JSON line from sample_clock's readings. A
+    reading whose peak at that clock is below what the dominant kernel was
+    measured to reach cannot be the clock it ran at (amd-smi can report a
+    stale or idle value while short kernels run): the figures are then left
+    out and the record says why."""
+    ghz = clk[0]
+    peak_at_clock = (PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_FP32_TFLOPS) * ghz / 2.4
+    rec = {"source": "amd-smi metric --clock (GFX clock averaged over the XCDs) while "
+                     "steps ran back to back after the timed region",
+           "GHz": ghz, "GHz_min": clk[1], "GHz_max": clk[2], "readings": clk[3]}
+    if achieved > peak_at_clock:
+        rec.update(GHz=None, discarded_GHz=ghz,
+                   note="readings below the clock the measured throughput needs; discarded")
+        return rec
+    rec.update(peak_at_clock=peak_at_clock,
+               end_to_end_frac_at_clock=gemm_flops(case) / (ms / 1e3) / 1e12 / peak_at_clock,
+               roofline_frac_at_clock=achieved / peak_at_clock)
+    return rec
+
+
 def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
     """Time the oracle on two row samples and extrapolate to the full batch."""
     import numpy as np
@@ -325,16 +346,7 @@ def main():
         print("[bench] reading the shader clock while steps run", file=sys.stderr, flush=True)
         clk = sample_clock(step, torch.cuda.synchronize, ms)
         if clk:
-            ghz = clk[0]
-            peak_at_clock = PEAK_BF16_TFLOPS * ghz / 2.4 if case.dtype == "bf16" else \
-                PEAK_FP32_TFLOPS * ghz / 2.4
-            out["clock"] = {
-                "source": "amd-smi metric --clock (GFX clock averaged over the XCDs) while "
-                          "steps ran back to back after the timed region",
-                "GHz": ghz, "GHz_min": clk[1], "GHz_max": clk[2], "readings": clk[3],
-                "peak_at_clock": peak_at_clock,
-                "end_to_end_frac_at_clock": gemm_flops(case) / (ms / 1e3) / 1e12 / peak_at_clock,
-                "roofline_frac_at_clock": achieved / peak_at_clock}
+            out["clock"] = clock_record(clk, case, ms, achieved)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, case)

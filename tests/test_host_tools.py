@@ -198,3 +198,16 @@ def test_bench_json_line_on_the_gpu():
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
     assert 0.0 < r["frac"] < 1.0
     assert {"logits", "row", "dx", "prep", "final"} <= set(d["kernels"])
+
+
+def test_clock_record_discards_impossible_readings():
+    case = workloads.CONFIGS[3]
+    ms = 13.0
+    # 1300 TFLOP/s needs at least 1300/2500*2.4 = 1.25 GHz
+    ok = bench.clock_record((1.8, 1.7, 1.9, 6), case, ms, 1300.0)
+    assert ok["GHz"] == 1.8
+    assert ok["roofline_frac_at_clock"] == pytest.approx(1300.0 / (bench.PEAK_BF16_TFLOPS * 0.75))
+    assert 0 < ok["end_to_end_frac_at_clock"] < 1
+    bad = bench.clock_record((0.2, 0.2, 0.2, 6), case, ms, 1300.0)
+    assert bad["GHz"] is None and bad["discarded_GHz"] == 0.2
+    assert "roofline_frac_at_clock" not in bad
