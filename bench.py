@@ -240,7 +240,7 @@ def main():
     import lm_head_projection_token_amd as fll
     import workloads
 
-    case = workloads.JSD_WORKLOAD if args.config == "jsd" else workloads.CONFIGS[int(args.config)]
+    case = workloads.JSD_WORKLOAD if args.config == "jsd" else workloads.WORKLOADS[int(args.config)]
     inp = workloads.make_inputs(case)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

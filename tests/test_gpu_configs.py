@@ -25,13 +25,13 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
 def test_cfg1_full():
-    case = workloads.CONFIGS[1]
+    case = workloads.WORKLOADS[1]
     inp = H.make(case)
     H.compare_full(H.run_gpu(inp, case), H.run_oracle(inp, case), case)
 
 
 def test_cfg2_full():
-    case = workloads.CONFIGS[2]
+    case = workloads.WORKLOADS[2]
     print(f"[cfg2] {case}", flush=True)
     inp = H.make(case)
     out = H.run_gpu(inp, case)
@@ -41,7 +41,7 @@ def test_cfg2_full():
 
 # The fused linear cross-entropy head at the llama-3 head shape of the
 # V=128256 GRPO workload, with a trainable head (beyond the five workloads).
-CE_FULL = workloads.CONFIGS[3].replace(name="ce-bf16-trainable-B8T1024-V128256", head="ce",
+CE_FULL = workloads.WORKLOADS[3].replace(name="ce-bf16-trainable-B8T1024-V128256", head="ce",
                                        compute_dW=True, ignore_frac=0.05, seed=6)
 EXTRA = {"ce": CE_FULL, "jsd": workloads.JSD_WORKLOAD}
 
@@ -53,7 +53,7 @@ def test_full_config_sampled(cfg):
     logits_bf16 = isinstance(cfg, str) and cfg.endswith("-bf16-logits")
     key = cfg[:-len("-bf16-logits")] if logits_bf16 else cfg
     key = int(key) if isinstance(key, str) and key.isdigit() else key
-    case = EXTRA[key] if key in EXTRA else workloads.CONFIGS[key]
+    case = EXTRA[key] if key in EXTRA else workloads.WORKLOADS[key]
     print(f"[cfg{cfg}] {case}", flush=True)
     inp = H.make(case)
     out = H.run_gpu(inp, case, logits_bf16=logits_bf16)

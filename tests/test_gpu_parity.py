@@ -20,7 +20,7 @@ from tests import helpers as H
 pytestmark = pytest.mark.gpu
 
 SMALL = {
-    "cfg1-tiny-fp32-kl": workloads.CONFIGS[1],
+    "cfg1-tiny-fp32-kl": workloads.WORKLOADS[1],
     "kl-bf16-ragged-trainable-bias": workloads.small_case(
         BT=300, H=264, V=1000, dtype="bf16", head="kl", has_bias=True, compute_dW=True,
         compute_db=True, temperature=2.0, ignore_frac=0.1, reduction="batchmean",

@@ -31,8 +31,8 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_bench_flops_follow_the_gradient_flags():
-    frozen = workloads.CONFIGS[3]
-    trainable = workloads.CONFIGS[5]
+    frozen = workloads.WORKLOADS[3]
+    trainable = workloads.WORKLOADS[5]
     per = 2.0 * frozen.BT * frozen.H * frozen.V
     # logits and dX only when frozen; dW adds a third product
     assert bench.gemm_flops(frozen) == 2 * per
@@ -44,16 +44,16 @@ def test_bench_flops_follow_the_gradient_flags():
 
 
 def test_bench_row_bytes_per_valid_row():
-    V = workloads.CONFIGS[3].V
+    V = workloads.WORKLOADS[3].V
     # selective: read fp32 logits, write bf16 dlogits; KL also reads the fp32 target
-    assert bench.row_bytes_per_valid_row(workloads.CONFIGS[3]) == 6 * V
-    assert bench.row_bytes_per_valid_row(workloads.CONFIGS[5]) == 10 * V
-    assert bench.row_bytes_per_valid_row(workloads.CONFIGS[3], logits_bf16=True) == 4 * V
+    assert bench.row_bytes_per_valid_row(workloads.WORKLOADS[3]) == 6 * V
+    assert bench.row_bytes_per_valid_row(workloads.WORKLOADS[5]) == 10 * V
+    assert bench.row_bytes_per_valid_row(workloads.WORKLOADS[3], logits_bf16=True) == 4 * V
     assert bench.row_bytes_per_valid_row(workloads.JSD_WORKLOAD) == 10 * V
 
 
 def test_measured_traffic_needs_matching_sources(tmp_path, monkeypatch):
-    case = workloads.CONFIGS[3]
+    case = workloads.WORKLOADS[3]
     prof = tmp_path / "profiles"
     prof.mkdir()
     rec = {"src_sha256": profiling.source_hash(),
@@ -201,7 +201,7 @@ def test_bench_json_line_on_the_gpu():
 
 
 def test_clock_record_discards_impossible_readings():
-    case = workloads.CONFIGS[3]
+    case = workloads.WORKLOADS[3]
     ms = 13.0
     # 1300 TFLOP/s needs at least 1300/2500*2.4 = 1.25 GHz
     ok = bench.clock_record((1.8, 1.7, 1.9, 6), case, ms, 1300.0)

@@ -73,7 +73,7 @@ class Case:
 
 
 # The five workloads. Seeds are the case numbers.
-CONFIGS = {
+WORKLOADS = {
     1: Case("tiny-fp32-kl-trainable-bias", BT=64, H=256, V=1024, dtype="fp32",
             head=HEAD_KL, has_bias=True, compute_dW=True, compute_db=True,
             reduction="batchmean", x_std=0.02, w_std=0.02, b_std=0.01,
