@@ -152,7 +152,8 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_b
 
 
 N_XCD = 8
-N_SIMD = 256 * 4
+N_CU = 256
+N_SIMD = N_CU * 4
 PEAK_CLOCK_GHZ = 2.4
 FLOP_PER_CLK_SIMD_BF16 = 1024  # dense bf16: 256 CU x 4 SIMD x 1024 x 2.4 GHz = 2516.6 TFLOP/s
 
@@ -231,6 +232,55 @@ def mfma_summary(d, workload, command, out_base) -> None:
         fh.write("\n".join(lines))
 
 
+def lds_summary(d, workload, command, out_base) -> None:
+    """Per kernel kind (median over dispatches): LDS instructions issued per
+    CU, the cycles the LDS spent on indexed (ds_read / ds_write) work and the
+    cycles it stalled on bank conflicts, both per CU, and conflicts as a
+    fraction of the indexed cycles."""
+    names = ("SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT")
+    vals = defaultdict(lambda: defaultdict(float))
+    kname = {}
+    for r in _counter_rows(d):
+        n = r["Counter_Name"]
+        if n in names:
+            vals[int(r["Dispatch_Id"])][n] += float(r["Counter_Value"])
+            kname[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    per_kind = defaultdict(list)
+    for did, c in vals.items():
+        kind = kernel_kind(kname[did])
+        if kind is None or any(n not in c for n in names):
+            continue
+        idx = c["SQ_LDS_IDX_ACTIVE"]
+        per_kind[kind].append({"lds_insts_per_cu": c["SQ_INSTS_LDS"] / N_CU,
+                               "idx_active_per_cu": idx / N_CU,
+                               "bank_conflict_per_cu": c["SQ_LDS_BANK_CONFLICT"] / N_CU,
+                               "conflict_frac": c["SQ_LDS_BANK_CONFLICT"] / idx if idx else 0.0})
+    kinds = {}
+    for kind, rows in per_kind.items():
+        kinds[kind] = {k: statistics.median(r[k] for r in rows) for k in rows[0]}
+        kinds[kind]["dispatches"] = len(rows)
+    rec = {"workload": workload, "command": command, "src_sha256": source_hash(),
+           "kernels": kinds}
+    with open(out_base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = [f"# LDS bank conflicts: {workload}", "",
+             f"Command (from the repository root): `{command}`", "",
+             "Per dispatch, divided by 256 CUs: SQ_INSTS_LDS (LDS instructions issued), "
+             "SQ_LDS_IDX_ACTIVE (cycles of indexed LDS work), SQ_LDS_BANK_CONFLICT "
+             "(cycles stalled on bank conflicts); conflict share = bank-conflict cycles / "
+             "indexed cycles. Medians over dispatches.", "",
+             "| kernel | dispatches | LDS insts per CU | indexed cycles per CU | "
+             "conflict cycles per CU | conflict share |",
+             "|---|---|---|---|---|---|"]
+    for k, v in sorted(kinds.items(), key=lambda kv: -kv[1]["idx_active_per_cu"]):
+        lines.append(f"| {k} | {v['dispatches']} | {v['lds_insts_per_cu']:.0f} | "
+                     f"{v['idx_active_per_cu']:.0f} | {v['bank_conflict_per_cu']:.0f} | "
+                     f"{100 * v['conflict_frac']:.2f}% |")
+    lines += ["", f"Kernel sources sha256: `{rec['src_sha256']}`", ""]
+    with open(out_base + ".md", "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -248,8 +298,13 @@ def main():
     m = sub.add_parser("mfma")
     for a in ("--dir", "--workload", "--command", "--out"):
         m.add_argument(a, required=True)
+    ls = sub.add_parser("lds")
+    for a in ("--dir", "--workload", "--command", "--out"):
+        ls.add_argument(a, required=True)
     args = ap.parse_args()
-    if args.cmd == "kernels":
+    if args.cmd == "lds":
+        lds_summary(args.dir, args.workload, args.command, args.out)
+    elif args.cmd == "kernels":
         kernels_summary(args.stats, args.workload, args.command, args.out, args.note)
     elif args.cmd == "mfma":
         mfma_summary(args.dir, args.workload, args.command, args.out)

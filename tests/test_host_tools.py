@@ -211,3 +211,28 @@ def test_clock_record_discards_impossible_readings():
     bad = bench.clock_record((0.2, 0.2, 0.2, 6), case, ms, 1300.0)
     assert bad["GHz"] is None and bad["discarded_GHz"] == 0.2
     assert "roofline_frac_at_clock" not in bad
+
+
+def test_lds_summary_per_cu_and_conflict_share(tmp_path):
+    d = tmp_path / "l"
+    d.mkdir()
+    rows = []
+    for did, scale in ((3, 1.0), (7, 1.2), (11, 0.8)):
+        for name, val in (("SQ_INSTS_LDS", 1000.0 * 256), ("SQ_LDS_IDX_ACTIVE", 4000.0 * 256),
+                          ("SQ_LDS_BANK_CONFLICT", 40.0 * 256)):
+            # each counter split over two instances of the dispatch
+            for half in (0.5, 0.5):
+                rows.append({"Dispatch_Id": did, "Kernel_Name": LOGITS, "Counter_Name": name,
+                             "Counter_Value": val * scale * half})
+    rows.append({"Dispatch_Id": 20, "Kernel_Name": ROW, "Counter_Name": "SQ_INSTS_LDS",
+                 "Counter_Value": 5.0})
+    _write_counters(d / "l_counter_collection.csv", rows)
+    profiling.lds_summary(str(d), "x", "cmd", str(tmp_path / "lds_x"))
+    rec = json.loads((tmp_path / "lds_x.json").read_text())["kernels"]
+    k = rec["logits"]
+    assert k["dispatches"] == 3
+    assert k["lds_insts_per_cu"] == pytest.approx(1000.0)
+    assert k["idx_active_per_cu"] == pytest.approx(4000.0)
+    assert k["conflict_frac"] == pytest.approx(0.01)
+    assert "row" not in rec  # a dispatch without every counter is left out
+    assert "| logits | 3 |" in (tmp_path / "lds_x.md").read_text()
