@@ -281,6 +281,54 @@ def lds_summary(d, workload, command, out_base) -> None:
         fh.write("\n".join(lines))
 
 
+def ta_summary(d, workload, command, out_base) -> None:
+    """Per kernel kind (median over dispatches): the fraction of active
+    cycles the texture-address (TA) unit of a CU is busy, TA_BUSY_avr (TA
+    busy cycles averaged over the TA instances) over GRBM_GUI_ACTIVE / 8 XCDs,
+    and the buffer-instruction share of those cycles,
+    TA_BUFFER_TOTAL_CYCLES_sum / (TA_BUSY_avr x 256 instances)."""
+    names = ("TA_BUSY_avr", "TA_BUFFER_TOTAL_CYCLES_sum", "GRBM_GUI_ACTIVE")
+    vals = defaultdict(lambda: defaultdict(float))
+    kname = {}
+    for r in _counter_rows(d):
+        n = r["Counter_Name"]
+        if n in names:
+            vals[int(r["Dispatch_Id"])][n] += float(r["Counter_Value"])
+            kname[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    per_kind = defaultdict(list)
+    for did, c in vals.items():
+        kind = kernel_kind(kname[did])
+        if kind is None or any(n not in c for n in names):
+            continue
+        active = c["GRBM_GUI_ACTIVE"] / N_XCD
+        busy = c["TA_BUSY_avr"]
+        per_kind[kind].append({
+            "ta_busy_frac": busy / active if active else 0.0,
+            "buffer_share": c["TA_BUFFER_TOTAL_CYCLES_sum"] / (busy * N_CU) if busy else 0.0})
+    kinds = {}
+    for kind, rows in per_kind.items():
+        kinds[kind] = {k: statistics.median(r[k] for r in rows) for k in rows[0]}
+        kinds[kind]["dispatches"] = len(rows)
+    rec = {"workload": workload, "command": command, "src_sha256": source_hash(),
+           "kernels": kinds}
+    with open(out_base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = [f"# Texture-address unit busy: {workload}", "",
+             f"Command (from the repository root): `{command}`", "",
+             "Per dispatch: TA busy = TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8 XCDs), the share of "
+             "active cycles a CU's TA unit (address processing of every vector memory "
+             "instruction, LDS-DMA loads included) is busy; buffer share = "
+             "TA_BUFFER_TOTAL_CYCLES_sum / (TA_BUSY_avr x 256). Medians over dispatches.", "",
+             "| kernel | dispatches | TA busy | buffer share of TA cycles |",
+             "|---|---|---|---|"]
+    for k, v in sorted(kinds.items(), key=lambda kv: -kv[1]["ta_busy_frac"]):
+        lines.append(f"| {k} | {v['dispatches']} | {100 * v['ta_busy_frac']:.1f}% | "
+                     f"{100 * v['buffer_share']:.1f}% |")
+    lines += ["", f"Kernel sources sha256: `{rec['src_sha256']}`", ""]
+    with open(out_base + ".md", "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -301,8 +349,13 @@ def main():
     ls = sub.add_parser("lds")
     for a in ("--dir", "--workload", "--command", "--out"):
         ls.add_argument(a, required=True)
+    ta = sub.add_parser("ta")
+    for a in ("--dir", "--workload", "--command", "--out"):
+        ta.add_argument(a, required=True)
     args = ap.parse_args()
-    if args.cmd == "lds":
+    if args.cmd == "ta":
+        ta_summary(args.dir, args.workload, args.command, args.out)
+    elif args.cmd == "lds":
         lds_summary(args.dir, args.workload, args.command, args.out)
     elif args.cmd == "kernels":
         kernels_summary(args.stats, args.workload, args.command, args.out, args.note)

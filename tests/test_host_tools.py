@@ -236,3 +236,20 @@ def test_lds_summary_per_cu_and_conflict_share(tmp_path):
     assert k["conflict_frac"] == pytest.approx(0.01)
     assert "row" not in rec  # a dispatch without every counter is left out
     assert "| logits | 3 |" in (tmp_path / "lds_x.md").read_text()
+
+
+def test_ta_summary_busy_fraction(tmp_path):
+    d = tmp_path / "a"
+    d.mkdir()
+    rows = []
+    for did in (2, 4):
+        for name, val in (("GRBM_GUI_ACTIVE", 8 * 1000.0), ("TA_BUSY_avr", 450.0),
+                          ("TA_BUFFER_TOTAL_CYCLES_sum", 0.8 * 450.0 * 256)):
+            rows.append({"Dispatch_Id": did, "Kernel_Name": LOGITS, "Counter_Name": name,
+                         "Counter_Value": val})
+    _write_counters(d / "a_counter_collection.csv", rows)
+    profiling.ta_summary(str(d), "x", "cmd", str(tmp_path / "ta_x"))
+    k = json.loads((tmp_path / "ta_x.json").read_text())["kernels"]["logits"]
+    assert k["ta_busy_frac"] == pytest.approx(0.45)
+    assert k["buffer_share"] == pytest.approx(0.8)
+    assert k["dispatches"] == 2
