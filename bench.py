@@ -89,8 +89,9 @@ def sample_clock(step, sync, ms_per_step, samples=6):
     --clock` is read a few times from a helper thread, each reading averaged
     over the GFX clock of every XCD. Steps are queued ~100 ms at a time so
     that the GPU does not idle between them while a reading is taken. Returns (mean, min, max) of the
-    readings and their count, or None if amd-smi is missing or prints no GFX clock. Each
-    reading is instantaneous, so the mean mixes GEMM and row-kernel phases;
+    readings and their count, or None if amd-smi is missing or prints no GFX clock. amd-smi
+    refreshes the figure slowly (readings of one run can repeat exactly), and
+    it mixes GEMM and row-kernel phases;
     the per-kernel clocks come from the counters (GRBM_COUNT)."""
     import re
     import shutil
