@@ -15,6 +15,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 
 import workloads  # noqa: E402
 from oracle import fll_oracle  # noqa: E402
+from tests import helpers  # noqa: E402
 
 CASES = {
     # KL distillation, bf16 inputs, trainable head with bias, ignored rows.
@@ -32,6 +33,17 @@ CASES = {
         BT=12, H=16, V=40, dtype="bf16", head="jsd", has_bias=True, compute_dW=True,
         compute_db=True, H_teacher=24, teacher_has_bias=True, teacher_w_std=0.3,
         temperature=2.0, ignore_frac=0.25, w_std=0.3, seed=10),
+    # PPO clipped surrogate with DAPO's wider upper clip, bf16 inputs,
+    # trainable head with bias, ignored rows; old log-probs = the oracle's
+    # log p(y) minus drawn log-ratios of spread 0.4 (both clip branches).
+    "ppo_bf16_small": workloads.small_case(
+        BT=14, H=16, V=40, dtype="bf16", head="ppo", has_bias=True, compute_dW=True,
+        compute_db=True, clip_low=0.2, clip_high=0.28, logratio_std=0.4,
+        temperature=2.0, ignore_frac=0.2, w_std=0.3, reduction="mean", seed=25),
+    # CISPO, fp32 inputs, frozen head, sum reduction.
+    "cispo_fp32_small": workloads.small_case(
+        BT=10, H=8, V=33, dtype="fp32", head="cispo", clip_low=0.2, clip_high=0.28,
+        logratio_std=0.4, reduction="sum", x_std=1.0, w_std=0.5, seed=26),
 }
 
 
@@ -49,7 +61,7 @@ def run_case(case):
         temperature=case.temperature, eps=case.eps,
         compute_dW=case.compute_dW, compute_db=case.compute_db,
         X_teacher=np_(inp["X_teacher"]), W_teacher=np_(inp["W_teacher"]),
-        b_teacher=np_(inp["b_teacher"]))
+        b_teacher=np_(inp["b_teacher"]), **helpers._ratio_kw(inp, case))
     rec = dict(loss=out["loss"], per_row=out["per_row"].tolist(),
                n_valid=out["n_valid"], dX_row0=out["dX"][0].tolist(),
                dX_sum=float(out["dX"].sum()))

@@ -12,14 +12,55 @@ Tolerances (stated for the method's float configurations):
 
 from __future__ import annotations
 
+import math
+import sys
+import time
+
 import numpy as np
 import torch
 
 import workloads
 
+RATIO_MARGIN = 1e-3  # log-ratios kept this far from the clip edges (see below)
+
 
 def to_np(t):
     return None if t is None else t.detach().cpu().double().numpy()
+
+
+def ratio_old_logprobs(inp, case, margin=RATIO_MARGIN, block_rows=512):
+    """The ratio heads' old log-probs: old_r = log p(y_r) - d_r, with log p(y_r)
+    from the oracle and d_r the drawn log-ratio, as float32 (the GPU's input;
+    the oracle then reads the same values). A drawn d_r within ``margin`` of a
+    clip edge (log(1 + clip_high), log(1 - clip_low)) is moved 2 * margin
+    away from it: there the clip decision turns on the last bits of log p(y),
+    which float32 logits on the GPU and float64 ones in the oracle need not
+    share, and either branch would be right. Cached in ``inp``."""
+    if inp.get("old_logprobs") is not None:
+        return inp["old_logprobs"]
+    from oracle import fll_oracle
+
+    d = inp["logratio"].double().numpy().copy()
+    edges = [math.log1p(case.clip_high)]
+    if case.clip_low < 1.0:
+        edges.append(math.log1p(-case.clip_low))
+    for e in edges:
+        near = np.abs(d - e) < margin
+        d[near] = e + np.where(d[near] >= e, 2 * margin, -2 * margin)
+    labels = inp["labels"].numpy()
+    lp = fll_oracle.label_logprobs(
+        to_np32(inp["X"]), to_np32(inp["W"]), to_np(inp["b"]), labels,
+        temperature=case.temperature, ignore_index=case.ignore_index,
+        block_rows=block_rows)
+    old = torch.from_numpy((lp - d).astype(np.float32))
+    old[inp["labels"] == case.ignore_index] = float("nan")  # never read
+    inp["old_logprobs"] = old
+    return old
+
+
+def to_np32(t):
+    """float32 numpy view of a CPU tensor (bf16 and fp32 values are exact)."""
+    return None if t is None else t.detach().cpu().float().numpy()
 
 
 def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0", logits_bf16=False):
@@ -28,6 +69,11 @@ def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0", logits_bf16=
     def dev(t):
         return None if t is None else t.to(device).contiguous()
 
+    ratio = {}
+    if case.head in workloads.RATIO_HEADS:
+        ratio = dict(old_logprobs=dev(ratio_old_logprobs(inp, case)),
+                     clip_low=case.clip_low, clip_high=case.clip_high)
+
     out = fll.fused_lm_head_loss(
         dev(inp["X"]), dev(inp["W"]), dev(inp["b"]), head=case.head,
         labels=dev(inp["labels"]), target=dev(inp["target"]), weights=dev(inp["weights"]),
@@ -35,9 +81,43 @@ def run_gpu(inp, case, chunk_rows=0, per_row=True, device="cuda:0", logits_bf16=
         temperature=case.temperature, eps=case.eps, compute_dW=case.compute_dW,
         compute_db=case.compute_db, chunk_rows=chunk_rows, per_row=per_row,
         X_teacher=dev(inp.get("X_teacher")), W_teacher=dev(inp.get("W_teacher")),
-        b_teacher=dev(inp.get("b_teacher")), logits_bf16=logits_bf16)
+        b_teacher=dev(inp.get("b_teacher")), logits_bf16=logits_bf16, **ratio)
     torch.cuda.synchronize()
     return out
+
+
+def _ratio_kw(inp, case):
+    if case.head not in workloads.RATIO_HEADS:
+        return {}
+    return dict(old_logprobs=to_np(ratio_old_logprobs(inp, case)),
+                clip_low=case.clip_low, clip_high=case.clip_high)
+
+
+def run_oracle_blocked(inp, case, block_rows=512, tag=""):
+    """The oracle's row-blocked pass over the whole batch (the same arithmetic
+    as ``fwd_bwd``), printing its progress every ~20 % of the rows."""
+    from oracle import fll_oracle
+
+    t0 = time.time()
+    marks = set()
+
+    def progress(done, total):
+        pct = int(100 * done / total) // 20 * 20
+        if pct not in marks:
+            marks.add(pct)
+            print(f"[oracle {tag}] {done}/{total} rows, {time.time() - t0:.0f} s",
+                  flush=True, file=sys.stderr)
+
+    return fll_oracle.fwd_bwd_blocked(
+        to_np32(inp["X"]), to_np32(inp["W"]), to_np(inp["b"]), head=case.head,
+        labels=None if inp["labels"] is None else inp["labels"].numpy(),
+        target=None if inp["target"] is None else inp["target"].numpy(),
+        weights=to_np(inp["weights"]), reduction=case.reduction,
+        ignore_index=case.ignore_index, temperature=case.temperature, eps=case.eps,
+        compute_dW=case.compute_dW, compute_db=case.compute_db,
+        X_teacher=to_np32(inp.get("X_teacher")), W_teacher=to_np32(inp.get("W_teacher")),
+        b_teacher=to_np(inp.get("b_teacher")), block_rows=block_rows, progress=progress,
+        **_ratio_kw(inp, case))
 
 
 def run_oracle(inp, case):
@@ -50,7 +130,8 @@ def run_oracle(inp, case):
         reduction=case.reduction, ignore_index=case.ignore_index,
         temperature=case.temperature, eps=case.eps, compute_dW=case.compute_dW,
         compute_db=case.compute_db, X_teacher=to_np(inp.get("X_teacher")),
-        W_teacher=to_np(inp.get("W_teacher")), b_teacher=to_np(inp.get("b_teacher")))
+        W_teacher=to_np(inp.get("W_teacher")), b_teacher=to_np(inp.get("b_teacher")),
+        **_ratio_kw(inp, case))
 
 
 def check_loss(gpu_loss: float, ref: float, dtype: str, what="loss"):
@@ -60,24 +141,45 @@ def check_loss(gpu_loss: float, ref: float, dtype: str, what="loss"):
         f"{what}: gpu {gpu_loss!r} vs oracle {ref!r} (rel {err / max(abs(ref), 1e-300):.3e})"
 
 
+def _row_blocks(n, elems_per_row, target=1 << 24):
+    step = max(1, target // max(1, elems_per_row))
+    return [slice(i, min(n, i + step)) for i in range(0, max(n, 1), step)]
+
+
 def check_grad(got, ref, dtype: str, what: str):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+    """Element-wise gradient check at the stated tolerances (see the module
+    docstring). Large arrays (a full V x H weight gradient) are compared in
+    row blocks with the same per-tensor scale and Frobenius norms, so no
+    temporary of the whole array's size is formed."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
     assert got.shape == ref.shape, what
-    assert np.isfinite(got).all(), f"{what}: non-finite values"
-    scale = float(np.abs(ref).max()) if ref.size else 0.0
-    if dtype == "fp32":
-        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5 * scale, err_msg=what)
+    if ref.size == 0:
         return
-    np.testing.assert_allclose(got, ref, rtol=2e-2, atol=1e-2, err_msg=what + " (stated)")
-    np.testing.assert_allclose(got, ref, rtol=2e-2, atol=1e-2 * scale,
-                               err_msg=what + " (scaled)")
-    den = np.linalg.norm(ref)
+    n = ref.shape[0]
+    per_row = int(ref.size // max(n, 1))
+    blocks = _row_blocks(n, per_row)
+    scale = max(float(np.abs(ref[blk]).max()) for blk in blocks)
+    num = den = 0.0
+    for blk in blocks:
+        g = np.asarray(got[blk], dtype=np.float64)
+        r = np.asarray(ref[blk], dtype=np.float64)
+        assert np.isfinite(g).all(), f"{what}: non-finite values"
+        if dtype == "fp32":
+            np.testing.assert_allclose(g, r, rtol=1e-5, atol=1e-5 * scale, err_msg=what)
+            continue
+        np.testing.assert_allclose(g, r, rtol=2e-2, atol=1e-2, err_msg=what + " (stated)")
+        np.testing.assert_allclose(g, r, rtol=2e-2, atol=1e-2 * scale,
+                                   err_msg=what + " (scaled)")
+        num += float(np.square(g - r).sum())
+        den += float(np.square(r).sum())
+    if dtype == "fp32":
+        return
     if den > 0:
-        rel = np.linalg.norm(got - ref) / den
+        rel = math.sqrt(num / den)
         assert rel <= 1e-2, f"{what}: relative Frobenius error {rel:.3e}"
     else:
-        assert np.abs(got).max() == 0.0, f"{what}: expected exact zeros"
+        assert num == 0.0, f"{what}: expected exact zeros"
 
 
 BF16_UNIT_ROUNDOFF = 2.0 ** -8

@@ -15,7 +15,8 @@ from tests import test_oracle_pins as P
 
 _orig = {name: getattr(O, name) for name in
          ("logits", "kl_rows", "selective_rows", "dlogits", "reduction_scale",
-          "valid_rows", "log_softmax", "jsd_rows", "teacher_probs")}
+          "valid_rows", "log_softmax", "jsd_rows", "teacher_probs", "ratio_rows",
+          "row_weights", "fwd_bwd_blocked")}
 
 
 def _kl_without_entropy(logP, target, valid, eps):
@@ -112,6 +113,79 @@ def _valid_all_rows(labels, ignore_index, BT):
     return np.ones(BT, dtype=bool)
 
 
+def _kl_no_zero_guard(logP, target, valid, eps):
+    L = np.zeros(logP.shape[0])
+    r = np.nonzero(valid)[0]
+    q = np.asarray(target, float)[r]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        L[r] = (q * np.log(np.maximum(q, eps)) - q * logP[r]).sum(axis=1)
+    return L
+
+
+def _ppo_takes_max(head, logP, labels, valid, old, A, lo, hi):
+    L, k = _orig["ratio_rows"](head, logP, labels, valid, old, A, lo, hi)
+    if head != "ppo":
+        return L, k
+    r = np.nonzero(valid)[0]
+    lp = logP[r, np.asarray(labels)[r]]
+    Ar = np.ones(r.size) if A is None else np.asarray(A, float)[r]
+    rho = np.exp(lp - np.asarray(old, float)[r])
+    c = np.clip(rho, 1 - lo, 1 + hi)
+    L[r] = -np.maximum(rho * Ar, c * Ar)
+    k[r] = np.where(rho * Ar >= c * Ar, -rho * Ar, 0.0)
+    return L, k
+
+
+def _ppo_clip_widths_swapped(head, logP, labels, valid, old, A, lo, hi):
+    return _orig["ratio_rows"](head, logP, labels, valid, old, A, hi, lo)
+
+
+def _ppo_grad_through_clip(head, logP, labels, valid, old, A, lo, hi):
+    L, k = _orig["ratio_rows"](head, logP, labels, valid, old, A, lo, hi)
+    if head == "ppo":
+        r = np.nonzero(valid)[0]
+        lp = logP[r, np.asarray(labels)[r]]
+        Ar = np.ones(r.size) if A is None else np.asarray(A, float)[r]
+        k[r] = -np.exp(lp - np.asarray(old, float)[r]) * Ar
+    return L, k
+
+
+def _ratio_inverted(head, logP, labels, valid, old, A, lo, hi):
+    # rho = exp(old - new): the old log-probs reflected about the new ones
+    r = np.nonzero(valid)[0]
+    lp = np.zeros(logP.shape[0])
+    lp[r] = logP[r, np.asarray(labels)[r]]
+    return _orig["ratio_rows"](head, logP, labels, valid, 2 * lp - np.asarray(old, float),
+                               A, lo, hi)
+
+
+def _cispo_grad_through_weight(head, logP, labels, valid, old, A, lo, hi):
+    L, k = _orig["ratio_rows"](head, logP, labels, valid, old, A, lo, hi)
+    if head == "cispo":
+        r = np.nonzero(valid)[0]
+        lp = logP[r, np.asarray(labels)[r]]
+        Ar = np.ones(r.size) if A is None else np.asarray(A, float)[r]
+        rho = np.exp(lp - np.asarray(old, float)[r])
+        inside = (rho > 1 - lo) & (rho < 1 + hi)
+        k[r] = k[r] - Ar * lp * rho * inside
+    return L, k
+
+
+def _ratio_weighted_twice(head, weights, BT):
+    if head in ("ppo", "cispo") and weights is not None:
+        return np.asarray(weights, float)
+    return _orig["row_weights"](head, weights, BT)
+
+
+def _blocked_drops_last_block(X, W, b=None, **kw):
+    out = _orig["fwd_bwd_blocked"](X, W, b, **kw)
+    blk = kw.get("block_rows", 512)
+    last = ((X.shape[0] - 1) // blk) * blk
+    if last > 0:
+        out["dX"][last:] = 0.0
+    return out
+
+
 MUTATIONS = {
     "kl drops sum q log q": ("kl_rows", _kl_without_entropy),
     "kl uses S - max": ("kl_rows", _kl_with_logits_not_logprobs),
@@ -131,6 +205,14 @@ MUTATIONS = {
     "JSD replaced by KL to the teacher": ("jsd_rows", _jsd_as_kl),
     "JSD gradient misses the mean term": ("dlogits", _dlogits_jsd_no_mean_term),
     "teacher logits not tempered": ("teacher_probs", _teacher_untempered),
+    "KL zero entries not guarded": ("kl_rows", _kl_no_zero_guard),
+    "PPO takes the max": ("ratio_rows", _ppo_takes_max),
+    "PPO clip widths swapped": ("ratio_rows", _ppo_clip_widths_swapped),
+    "PPO gradient through the clipped product": ("ratio_rows", _ppo_grad_through_clip),
+    "ratio inverted": ("ratio_rows", _ratio_inverted),
+    "CISPO gradient through its weight": ("ratio_rows", _cispo_grad_through_weight),
+    "ratio heads weighted twice": ("row_weights", _ratio_weighted_twice),
+    "blocked pass drops its last block": ("fwd_bwd_blocked", _blocked_drops_last_block),
 }
 
 
@@ -145,13 +227,16 @@ def _pin_tests():
         if not params:
             tests.append((name, fn, {}))
             continue
-        argnames, values = params[0].args[0], params[0].args[1]
-        names = [a.strip() for a in argnames.split(",")]
-        for v in values:
-            v = v if isinstance(v, tuple) else (v,)
-            if name == "test_gradients_central_differences" and v[2] != 2.0:
+        # stacked parametrize marks: every combination
+        combos = [{}]
+        for m in params:
+            names = [a.strip() for a in m.args[0].split(",")]
+            combos = [dict(c, **dict(zip(names, v if isinstance(v, tuple) else (v,))))
+                      for c in combos for v in m.args[1]]
+        for kw in combos:
+            if name == "test_gradients_central_differences" and kw["tau"] != 2.0:
                 continue  # one temperature suffices here; keeps the run short
-            tests.append((f"{name}{v}", fn, dict(zip(names, v))))
+            tests.append((f"{name}{tuple(kw.values())}", fn, kw))
     return tests
 
 

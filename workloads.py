@@ -30,6 +30,10 @@ HEAD_KL = "kl"
 HEAD_SELECTIVE = "selective"
 HEAD_CE = "ce"
 HEAD_JSD = "jsd"
+HEAD_PPO = "ppo"
+HEAD_CISPO = "cispo"
+LABEL_HEADS = (HEAD_SELECTIVE, HEAD_CE, HEAD_PPO, HEAD_CISPO)
+RATIO_HEADS = (HEAD_PPO, HEAD_CISPO)
 
 IGNORE_INDEX = -100
 
@@ -43,7 +47,7 @@ class Case:
     H: int
     V: int
     dtype: str  # "bf16" or "fp32"
-    head: str  # HEAD_KL, HEAD_SELECTIVE, HEAD_CE or HEAD_JSD
+    head: str  # HEAD_KL, HEAD_SELECTIVE, HEAD_CE, HEAD_JSD, HEAD_PPO or HEAD_CISPO
     has_bias: bool = False
     compute_dW: bool = False
     compute_db: bool = False
@@ -51,7 +55,7 @@ class Case:
     temperature: float = 1.0
     ignore_frac: float = 0.0
     with_labels: bool = True  # KL: labels act only as an ignore mask
-    with_weights: bool = True  # selective head: per-token advantages (never for CE)
+    with_weights: bool = True  # selective and ratio heads: per-token advantages (never CE)
     x_std: float = 1.0
     w_std: float = 0.02
     b_std: float = 0.01
@@ -63,6 +67,11 @@ class Case:
     H_teacher: int = 0
     teacher_has_bias: bool = False
     teacher_w_std: float = 0.02
+    # ratio heads: clip widths of the ratio rho and the spread of the drawn
+    # log-ratios log rho (the old log-probs are formed from them by the tests)
+    clip_low: float = 0.2
+    clip_high: float = 0.2
+    logratio_std: float = 0.3
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -114,7 +123,10 @@ def make_inputs(case: Case) -> dict:
     None (same dtype as X), ``target [BT,V]`` float32 or None, ``labels
     [BT]`` int64 or None, ``weights [BT]`` float32 or None, the JSD
     teacher's ``X_teacher [BT,H_t]``, ``W_teacher [V,H_t]``, ``b_teacher
-    [V]`` (else None), plus ``case``.
+    [V]`` (else None), the ratio heads' drawn log-ratios ``logratio [BT]``
+    float32 (else None), plus ``case``. The ratio heads' old log-probs depend
+    on the model's own log-probs, so the tests form them (old = log p(y) -
+    logratio, with log p(y) from the oracle); they are not drawn here.
     """
     gen = torch.Generator("cpu")
     gen.manual_seed(case.seed)
@@ -132,13 +144,13 @@ def make_inputs(case: Case) -> dict:
         del tl
 
     labels = None
-    need_labels = (case.head in (HEAD_SELECTIVE, HEAD_CE) or case.with_labels
+    need_labels = (case.head in LABEL_HEADS or case.with_labels
                    or case.ignore_frac > 0)
     if need_labels:
         labels = torch.randint(0, V, (BT,), generator=gen, dtype=torch.int64)
 
     weights = None
-    if case.head == HEAD_SELECTIVE and case.with_weights:
+    if case.head in (HEAD_SELECTIVE,) + RATIO_HEADS and case.with_weights:
         weights = _normal(gen, (BT,), 1.0)
 
     if case.ignore_frac > 0 and BT > 0:
@@ -157,8 +169,14 @@ def make_inputs(case: Case) -> dict:
         if case.teacher_has_bias:
             b_t = _normal(gen, (V,), case.b_std).to(dt)
 
+    # the ratio heads' per-token log-ratios log(pi / pi_old), drawn last
+    logratio = None
+    if case.head in RATIO_HEADS:
+        logratio = _normal(gen, (BT,), case.logratio_std)
+
     return dict(X=X, W=W, b=b, target=target, labels=labels, weights=weights,
-                X_teacher=X_t, W_teacher=W_t, b_teacher=b_t, case=case)
+                X_teacher=X_t, W_teacher=W_t, b_teacher=b_t, logratio=logratio,
+                case=case)
 
 
 def small_case(BT=300, H=264, V=1000, *, dtype="bf16", head=HEAD_KL, seed=100,
