@@ -9,7 +9,7 @@
  *   loss   = g * sum_r w_r * L_r                 (scalar, on the device)
  *   dX     = dZ W,  dW = dZ^T X,  db = sum_r dZ_r (dZ = d loss / d(X W^T + b))
  *
- * with one of four per-row heads:
+ * with one of six per-row heads:
  *
  *   FLL_HEAD_KL:                L_r = sum_v q_rv log(max(q_rv, eps)) - q_rv logP_rv
  *       KL(target || model) against an explicit target distribution q
@@ -24,6 +24,15 @@
  *       Pt = softmax((X_t W_t^T + b_t) / temperature), which takes no gradient
  *       [FusedLinearKLDivLoss page, Summary: the fused JSD loss whose teacher
  *       side needs its own projection]
+ *   FLL_HEAD_PPO_CLIP:          L_r = -min(rho_r A_r, clip(rho_r, 1 - clip_low,
+ *                                          1 + clip_high) A_r),
+ *       rho_r = exp(logP_{r, y_r} - old_r): the clipped surrogate of the GRPO
+ *       family built on the selective log-prob [frozen lm_head GRPO page,
+ *       Summary]; the published PPO objective, with DAPO's separate widths
+ *   FLL_HEAD_CISPO:             L_r = -sg(clip(rho_r, 1 - clip_low, 1 + clip_high))
+ *                                     A_r logP_{r, y_r},
+ *       the clipped ratio as a weight with no gradient through it (CISPO,
+ *       of the same family)
  *
  * The work runs in token chunks, and each chunk's gradient is formed inside
  * the same call (gradient-in-forward), so the BT x V logits are never
@@ -40,8 +49,10 @@
  *    allocates no device memory and keeps no pointer after a call returns.
  *  - All matrices are row-major and densely packed (row pitch = row length).
  *  - Status codes are fll_status values. Every argument is checked on the
- *    host before anything is enqueued, so an error return leaves every
- *    output untouched. fll_last_error() gives a thread-local message.
+ *    host before anything is enqueued, so an argument, support or workspace
+ *    error leaves every output untouched. FLL_ERR_HIP (a launch that failed)
+ *    can come after earlier kernels of the call were enqueued: the outputs
+ *    are then undefined. fll_last_error() gives a thread-local message.
  */
 #ifndef FLL_H
 #define FLL_H
@@ -53,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FLL_VERSION 3
+#define FLL_VERSION 4
 
 /* A hipStream_t, passed opaquely. NULL means the null (default) stream. */
 typedef void *fll_stream;
@@ -68,20 +79,29 @@ typedef enum {
 
 /* FLL_HEAD_CROSS_ENTROPY: L_r = -log p(y_r), optionally weighted by w_r --
  * the KL head against a one-hot target, i.e. the fused linear cross-entropy
- * loss whose chunk geometry the FusedLinearKLDivLoss page (Summary) reuses. */
+ * loss whose chunk geometry the FusedLinearKLDivLoss page (Summary) reuses.
+ * FLL_HEAD_PPO_CLIP and FLL_HEAD_CISPO (the ratio heads): the advantages A
+ * are `weights` (NULL = 1) and the old log-probs `old_logprobs`; the loss is
+ * g * sum_r L_r (A enters L_r, not as an outer weight). A tie of the PPO
+ * minimum (rho inside the clip range) takes the unclipped branch, whose
+ * gradient is -rho A (times d logP_y); the clipped branch has none.
+ * GRPO's per-sequence mean and Dr. GRPO's constant normaliser are positive
+ * per-token factors: fold them into A and use FLL_RED_SUM. */
 typedef enum {
   FLL_HEAD_KL = 0,
   FLL_HEAD_SELECTIVE_LOGPROB = 1,
   FLL_HEAD_CROSS_ENTROPY = 2,
-  FLL_HEAD_JSD = 3
+  FLL_HEAD_JSD = 3,
+  FLL_HEAD_PPO_CLIP = 4,
+  FLL_HEAD_CISPO = 5
 } fll_head;
 
 /* Reductions with the semantics of torch.nn.KLDivLoss
  * [FusedLinearKLDivLoss page, Details]. With n = the number of rows whose
  * label is not ignore_index (all rows when labels is NULL):
  *   BATCHMEAN: g = 1/n;  MEAN: g = 1/(n V) for KL and JSD, 1/n for the
- *   selective and cross-entropy heads (their tokens are the batch);  SUM: g = 1;
- *   n = 0 gives g = 0.
+ *   label heads (selective, cross-entropy, ratio: their tokens are the
+ *   batch; the token mean of DAPO and BNPO);  SUM: g = 1;  n = 0 gives g = 0.
  * NONE is refused with FLL_ERR_UNSUPPORTED: gradient-in-forward needs a
  * scalar loss [FusedLinearKLDivLoss page, Details]. */
 typedef enum {
@@ -109,7 +129,8 @@ typedef struct {
   int64_t ignore_index; /* label value marking a row as ignored (e.g. -100)  */
   float temperature;    /* > 0, finite; divides the model logits (and, for
                            JSD, the teacher's logits)                         */
-  float eps;            /* >= 0, finite; KL clamps q inside log(q) only       */
+  float eps;            /* >= 0, finite; KL clamps q inside log(q) only; an
+                           entry with q = 0 adds exactly 0 (eps = 0 too)      */
   int64_t H_teacher;    /* JSD: the teacher's hidden size, >= 8 and a multiple
                            of 8; every other head: 0                          */
   int32_t teacher_has_bias; /* JSD: 0/1, b_teacher is given; otherwise 0      */
@@ -124,6 +145,10 @@ typedef struct {
                            the fp32 chunk temporaries the method describes
                            [FusedLinearKLDivLoss page, Details] and is the
                            default. fp32 problems: 0.                        */
+  float clip_low;       /* ratio heads: the ratio is clipped to
+                           [1 - clip_low, 1 + clip_high]; 0 <= clip_low <= 1  */
+  float clip_high;      /* ratio heads: >= 0, +inf allowed (no upper clip).
+                           Every other head: both 0.                          */
 } fll_problem;
 
 /* The plan: a value type (nothing to free). Its fields after `p` are the
@@ -135,7 +160,8 @@ typedef struct {
   int64_t n_chunks;       /* ceil(BT / C)                                   */
   int64_t s_pitch;        /* elements per row of the chunk's logits buffer
                              (fp32, or bf16 with logits_bf16)               */
-  int64_t dx_splits;      /* dX split over the vocabulary (depends on V only)*/
+  int64_t dx_splits;      /* dX split over the vocabulary: depends on V, H and
+                             the chunk size, never on compute_dW/compute_db */
   int64_t dx_split_len;   /* vocabulary columns per dX split                */
   int64_t stat_tiles;     /* per-row statistics tiles (logits GEMM columns) */
   size_t off_logits;      /* workspace byte offsets                         */
@@ -153,28 +179,34 @@ typedef struct {
   const void *X;       /* [BT x H], dtype                                     */
   const void *W;       /* [V x H], dtype                                      */
   const void *b;       /* [V], dtype; NULL iff has_bias == 0                  */
-  const int64_t *labels; /* [BT]. SELECTIVE, CROSS_ENTROPY: required, values
-                            in [0, V) or ignore_index. KL, JSD: optional row
-                            mask (a row is ignored iff its label == ignore_index). */
+  const int64_t *labels; /* [BT]. SELECTIVE, CROSS_ENTROPY, ratio heads:
+                            required, values in [0, V) or ignore_index. KL,
+                            JSD: optional row mask (a row is ignored iff its
+                            label == ignore_index).                           */
   const float *target; /* KL: [BT x V] fp32 target probabilities, required.
                           Rows of ignored tokens are never read. Other heads:
                           NULL.                                               */
   const float *weights; /* SELECTIVE, CROSS_ENTROPY: [BT] fp32 per-token
-                           weights (advantages); NULL means all 1. KL, JSD: NULL. */
+                           weights (advantages); ratio heads: the advantages
+                           A; NULL means all 1. KL, JSD: NULL.                */
   void *dX;            /* [BT x H], dtype: written (every row, ignored = 0)    */
   float *dW;           /* [V x H] fp32: written iff compute_dW, else untouched
                           and may be NULL                                     */
   float *db;           /* [V] fp32: written iff compute_db, else untouched    */
   float *loss;         /* [1] fp32: written                                   */
   float *per_row;      /* optional [BT] fp32: KL_r (KL), log p(y_r)
-                          (SELECTIVE), -log p(y_r) (CROSS_ENTROPY) or JS_r
-                          (JSD) before weighting; 0 on ignored rows          */
+                          (SELECTIVE), -log p(y_r) (CROSS_ENTROPY), JS_r
+                          (JSD) before weighting, or the ratio heads' L_r;
+                          0 on ignored rows                                  */
   void *workspace;     /* >= plan.workspace_bytes, 256-byte aligned; contents
                           are scratch and need no initialisation              */
   size_t workspace_bytes;
   const void *X_teacher; /* JSD: [BT x H_teacher], dtype, 16-byte aligned; else NULL */
   const void *W_teacher; /* JSD: [V x H_teacher], dtype, 16-byte aligned; else NULL  */
   const void *b_teacher; /* JSD: [V], dtype, iff teacher_has_bias; else NULL          */
+  const float *old_logprobs; /* ratio heads: [BT] fp32 log-probs of the labels
+                                under the policy that sampled them (read on
+                                non-ignored rows only); else NULL            */
 } fll_args;
 
 /* Plan a problem: choose the token-chunk size and the workspace layout.
@@ -207,7 +239,7 @@ int fll_plan(const fll_problem *problem, size_t max_workspace_bytes,
  * dW / db kernels are launched only when compute_dW / compute_db are set
  * [frozen lm_head GRPO page, Summary; LoRA normalization page, Key Changes].
  *
- * A non-ignored label outside [0, V) (SELECTIVE, CROSS_ENTROPY) is not a
+ * A non-ignored label outside [0, V) (a label head) is not a
  * memory error: that row's per_row value and the loss become NaN and its
  * dlogits are zero. Calls that share a workspace must be ordered on one
  * stream.

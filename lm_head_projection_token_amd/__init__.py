@@ -22,6 +22,7 @@ from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfll.so")
+ABI_VERSION = 4  # FLL_VERSION of include/fll.h that the structs below mirror
 
 FLL_OK = 0
 FLL_ERR_INVALID_ARG = -1
@@ -33,8 +34,12 @@ FLL_HEAD_KL = 0
 FLL_HEAD_SELECTIVE_LOGPROB = 1
 FLL_HEAD_CROSS_ENTROPY = 2
 FLL_HEAD_JSD = 3
+FLL_HEAD_PPO_CLIP = 4
+FLL_HEAD_CISPO = 5
 HEADS = {"kl": FLL_HEAD_KL, "selective": FLL_HEAD_SELECTIVE_LOGPROB,
-         "ce": FLL_HEAD_CROSS_ENTROPY, "jsd": FLL_HEAD_JSD}
+         "ce": FLL_HEAD_CROSS_ENTROPY, "jsd": FLL_HEAD_JSD, "ppo": FLL_HEAD_PPO_CLIP,
+         "cispo": FLL_HEAD_CISPO}
+RATIO_HEADS = ("ppo", "cispo", FLL_HEAD_PPO_CLIP, FLL_HEAD_CISPO)
 
 FLL_RED_BATCHMEAN, FLL_RED_MEAN, FLL_RED_SUM, FLL_RED_NONE = 0, 1, 2, 3
 REDUCTIONS = {"batchmean": 0, "mean": 1, "sum": 2, "none": 3}
@@ -55,6 +60,7 @@ class FllProblem(ctypes.Structure):
         ("ignore_index", ctypes.c_int64), ("temperature", ctypes.c_float),
         ("eps", ctypes.c_float), ("H_teacher", ctypes.c_int64),
         ("teacher_has_bias", ctypes.c_int32), ("logits_bf16", ctypes.c_int32),
+        ("clip_low", ctypes.c_float), ("clip_high", ctypes.c_float),
     ]
 
 
@@ -80,7 +86,7 @@ class FllArgs(ctypes.Structure):
         ("loss", ctypes.c_void_p), ("per_row", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("X_teacher", ctypes.c_void_p), ("W_teacher", ctypes.c_void_p),
-        ("b_teacher", ctypes.c_void_p),
+        ("b_teacher", ctypes.c_void_p), ("old_logprobs", ctypes.c_void_p),
     ]
 
 
@@ -121,6 +127,9 @@ def _load():
     lib.fll_profile_enable.restype = ctypes.c_int
     lib.fll_profile_read.argtypes = [ctypes.POINTER(FllProfile), ctypes.c_int]
     lib.fll_profile_read.restype = ctypes.c_int
+    if lib.fll_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.fll_version()}, this binding "
+                          f"needs {ABI_VERSION}: rebuild it")
     return lib
 
 
@@ -155,14 +164,22 @@ def _check(status: int):
 def make_problem(BT, H, V, *, dtype="bf16", head="kl", has_bias=False, compute_dW=False,
                  compute_db=False, reduction="batchmean", ignore_index=-100,
                  temperature=1.0, eps=1e-10, H_teacher=0,
-                 teacher_has_bias=False, logits_bf16=False) -> FllProblem:
+                 teacher_has_bias=False, logits_bf16=False, clip_low=None,
+                 clip_high=None) -> FllProblem:
+    """The ratio heads' clip widths default to 0.2 each; other heads take 0."""
+    ratio = head in RATIO_HEADS
+    if clip_low is None:
+        clip_low = 0.2 if ratio else 0.0
+    if clip_high is None:
+        clip_high = 0.2 if ratio else 0.0
     return FllProblem(
         BT=BT, H=H, V=V, dtype=DTYPES[dtype] if isinstance(dtype, str) else dtype,
         head=HEADS[head] if isinstance(head, str) else head,
         has_bias=int(has_bias), compute_dW=int(compute_dW), compute_db=int(compute_db),
         reduction=REDUCTIONS[reduction] if isinstance(reduction, str) else reduction,
         ignore_index=ignore_index, temperature=temperature, eps=eps, H_teacher=H_teacher,
-        teacher_has_bias=int(teacher_has_bias), logits_bf16=int(logits_bf16))
+        teacher_has_bias=int(teacher_has_bias), logits_bf16=int(logits_bf16),
+        clip_low=clip_low, clip_high=clip_high)
 
 
 def fll_plan(problem: FllProblem, max_workspace_bytes: int = 0,
@@ -185,7 +202,7 @@ def _ptr(t) -> Optional[int]:
 def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weights=None,
                 dX, dW=None, db=None, loss, per_row=None, workspace,
                 workspace_bytes: Optional[int] = None, stream=None, X_teacher=None,
-                W_teacher=None, b_teacher=None) -> None:
+                W_teacher=None, b_teacher=None, old_logprobs=None) -> None:
     """Enqueue one fused forward + backward on ``stream`` (torch stream,
     raw handle int, or None for torch's current stream). Tensors must be
     contiguous device tensors of the dtypes ``include/fll.h`` states."""
@@ -195,7 +212,7 @@ def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weight
                     ("weights", weights), ("dX", dX), ("dW", dW), ("db", db),
                     ("loss", loss), ("per_row", per_row), ("workspace", workspace),
                     ("X_teacher", X_teacher), ("W_teacher", W_teacher),
-                    ("b_teacher", b_teacher)):
+                    ("b_teacher", b_teacher), ("old_logprobs", old_logprobs)):
         if isinstance(t, torch.Tensor) and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if workspace_bytes is None:
@@ -206,7 +223,7 @@ def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weight
                    db=_ptr(db), loss=_ptr(loss), per_row=_ptr(per_row),
                    workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
                    X_teacher=_ptr(X_teacher), W_teacher=_ptr(W_teacher),
-                   b_teacher=_ptr(b_teacher))
+                   b_teacher=_ptr(b_teacher), old_logprobs=_ptr(old_logprobs))
     if stream is None:
         handle = torch.cuda.current_stream().cuda_stream
     elif isinstance(stream, int):
@@ -230,11 +247,14 @@ def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=
                        reduction="batchmean", ignore_index=-100, temperature=1.0, eps=1e-10,
                        compute_dW=False, compute_db=False, chunk_rows=0, per_row=False,
                        workspace=None, X_teacher=None, W_teacher=None, b_teacher=None,
-                       logits_bf16=False):
+                       logits_bf16=False, old_logprobs=None, clip_low=None,
+                       clip_high=None):
     """Allocate outputs with torch and run the fused loss. Returns a dict with
     loss (0-dim fp32 tensor), dX, dW, db and (if asked) per_row. The JSD head
-    takes the teacher's X_teacher [BT, H_t], W_teacher [V, H_t] (+ b_teacher).
-    logits_bf16 keeps the chunk logits in bf16 (bf16 inputs only)."""
+    takes the teacher's X_teacher [BT, H_t], W_teacher [V, H_t] (+ b_teacher);
+    the ratio heads ("ppo", "cispo") take old_logprobs [BT] fp32, the
+    advantages as weights and the clip widths. logits_bf16 keeps the chunk
+    logits in bf16 (bf16 inputs only)."""
     import torch
 
     dev = X.device
@@ -246,7 +266,7 @@ def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=
                         compute_dW=compute_dW, compute_db=compute_db, reduction=reduction,
                         ignore_index=ignore_index, temperature=temperature, eps=eps,
                         H_teacher=H_t, teacher_has_bias=b_teacher is not None,
-                        logits_bf16=logits_bf16)
+                        logits_bf16=logits_bf16, clip_low=clip_low, clip_high=clip_high)
     plan = fll_plan(prob, 0, chunk_rows)
     if workspace is None or workspace.numel() < plan.workspace_bytes:
         workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
@@ -260,6 +280,6 @@ def fused_lm_head_loss(X, W, b=None, *, head, labels=None, target=None, weights=
     fll_fwd_bwd(plan, X=X, W=W, b=b, labels=labels, target=target, weights=weights,
                 dX=out["dX"], dW=out["dW"], db=out["db"], loss=out["loss"],
                 per_row=out["per_row"], workspace=workspace, X_teacher=X_teacher,
-                W_teacher=W_teacher, b_teacher=b_teacher)
+                W_teacher=W_teacher, b_teacher=b_teacher, old_logprobs=old_logprobs)
     out["plan"] = plan
     return out

@@ -37,6 +37,11 @@ constexpr size_t kDefaultBudget = size_t(64) << 30;  // 64 GiB of 288 GB
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
+inline bool ratio_head(int h) { return h == FLL_HEAD_PPO_CLIP || h == FLL_HEAD_CISPO; }
+// heads whose per-row term is a function of log p(y_r) of a label
+inline bool label_head(int h) {
+  return h == FLL_HEAD_SELECTIVE_LOGPROB || h == FLL_HEAD_CROSS_ENTROPY || ratio_head(h);
+}
 
 int check_problem(const fll_problem *p) {
   if (!p) return fail(FLL_ERR_INVALID_ARG, "problem is NULL");
@@ -48,9 +53,16 @@ int check_problem(const fll_problem *p) {
     return fail(FLL_ERR_INVALID_ARG, "unknown reduction %d", p->reduction);
   if (p->dtype != FLL_BF16 && p->dtype != FLL_FP32)
     return fail(FLL_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-  if (p->head != FLL_HEAD_KL && p->head != FLL_HEAD_SELECTIVE_LOGPROB &&
-      p->head != FLL_HEAD_CROSS_ENTROPY && p->head != FLL_HEAD_JSD)
+  if (p->head < FLL_HEAD_KL || p->head > FLL_HEAD_CISPO)
     return fail(FLL_ERR_INVALID_ARG, "unknown head %d", p->head);
+  if (ratio_head(p->head)) {
+    if (!(p->clip_low >= 0.0f && p->clip_low <= 1.0f))
+      return fail(FLL_ERR_INVALID_ARG, "clip_low must lie in [0, 1]");
+    if (!(p->clip_high >= 0.0f))  // +inf allowed: no upper clip
+      return fail(FLL_ERR_INVALID_ARG, "clip_high must be >= 0");
+  } else if (p->clip_low != 0.0f || p->clip_high != 0.0f) {
+    return fail(FLL_ERR_INVALID_ARG, "clip_low and clip_high are for the ratio heads");
+  }
   if (p->head == FLL_HEAD_JSD) {
     if (p->H_teacher < 8 || p->H_teacher % 8 != 0 || p->H_teacher > (int64_t(1) << 20))
       return fail(FLL_ERR_INVALID_ARG,
@@ -199,11 +211,12 @@ int check_args(const fll_plan_t *pl, const fll_args *a) {
   if (!a->X || !a->W || !a->dX) return fail(FLL_ERR_INVALID_ARG, "X, W and dX are required");
   if (!aligned(a->X, 16) || !aligned(a->W, 16) || !aligned(a->dX, 16))
     return fail(FLL_ERR_INVALID_ARG, "X, W and dX must be 16-byte aligned");
-  if (p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY) {
-    if (!a->labels)
-      return fail(FLL_ERR_INVALID_ARG, "the selective and cross-entropy heads need labels");
+  if (label_head(p.head)) {
+    if (!a->labels) return fail(FLL_ERR_INVALID_ARG, "the label heads need labels");
     if (a->target)
       return fail(FLL_ERR_INVALID_ARG, "target given for a label head");
+    if (ratio_head(p.head) && !a->old_logprobs)
+      return fail(FLL_ERR_INVALID_ARG, "the ratio heads need old_logprobs");
   } else if (p.head == FLL_HEAD_KL) {
     if (!a->target) return fail(FLL_ERR_INVALID_ARG, "the KL head needs a target");
     if (a->weights) return fail(FLL_ERR_INVALID_ARG, "weights given for the KL head");
@@ -220,6 +233,10 @@ int check_args(const fll_plan_t *pl, const fll_args *a) {
     if (p.teacher_has_bias && !aligned(a->b_teacher, esz))
       return fail(FLL_ERR_INVALID_ARG, "b_teacher misaligned");
   }
+  if (!ratio_head(p.head) && a->old_logprobs)
+    return fail(FLL_ERR_INVALID_ARG, "old_logprobs is for the ratio heads");
+  if (a->old_logprobs && !aligned(a->old_logprobs, 4))
+    return fail(FLL_ERR_INVALID_ARG, "old_logprobs misaligned");
   if (p.head != FLL_HEAD_JSD && (a->X_teacher || a->W_teacher || a->b_teacher))
     return fail(FLL_ERR_INVALID_ARG, "teacher inputs are for the JSD head");
   if (p.head == FLL_HEAD_JSD && !p.teacher_has_bias && a->b_teacher)
@@ -330,8 +347,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   const size_t esz = bf16 ? 2 : 4;
   // bf16 chunk logits: the label heads take the label's logit in fp32 from
   // the logits GEMM, through the per-row buffer the row kernel then fills
-  const bool label_head = p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY;
-  float *label_logit = bf16 && p.logits_bf16 && label_head && a.labels ? rowval : nullptr;
+  float *label_logit = bf16 && p.logits_bf16 && label_head(p.head) && a.labels ? rowval : nullptr;
   const float inv_tau = 1.0f / p.temperature;
 
   if (p.BT == 0) {
@@ -406,6 +422,9 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       ra.T = T;
       ra.stats_t = stats_t;
       ra.label_logit = label_logit;
+      ra.old_logprobs = a.old_logprobs;
+      ra.clip_low = p.clip_low;
+      ra.clip_high = p.clip_high;
       Probe pr(FLL_K_ROW, s);
       fll::launch_row(ra, s);
     }
@@ -447,6 +466,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   }
   {
     Probe pr(FLL_K_FINAL, s);
+    // the ratio heads' advantages are inside their per-row terms already
     const bool weighted = p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY;
     fll::launch_finalize(rowval, weighted ? a.weights : nullptr, p.BT, sc, a.loss, s);
   }

@@ -25,7 +25,7 @@ struct DevScalars {
 // label_logit (or null): for each row m with a label y = labels[label_row0
 // + m] inside [0, N), the fp32 logit S[m, y] is written to
 // label_logit[label_row0 + m] (bf16 chunk logits keep the label's logit
-// exact for the selective and cross-entropy heads).
+// exact for the label heads: selective, cross-entropy and ratio).
 void launch_logits_bf16(const void *X, int64_t ldx, const void *W, int64_t ldw,
                         const void *b, float inv_tau, void *S, int64_t lds, int s_bf16,
                         float2 *stats, int64_t n_stat, int64_t M, int64_t N, int64_t K,
@@ -72,7 +72,8 @@ void launch_prep(const int64_t *labels, int64_t BT, int64_t ignore_index,
 // bf16. On return the first V entries of each row hold dZ = dS / tau: over
 // bf16 logits element for element; over fp32 logits bf16 packed at the start
 // of the row (bf16 pitch 2 * s_pitch) when dz_bf16, else fp32 in place.
-// rowval[r] receives KL_r or log p(y_r) (0 when ignored). T (JSD) has S's
+// rowval[r] receives the row's term: KL_r, log p(y_r), -log p(y_r), JS_r or
+// the ratio heads' L_r (0 when ignored). T (JSD) has S's
 // element type and pitch.
 struct RowArgs {
   float *S;
@@ -96,6 +97,8 @@ struct RowArgs {
   const float *T;         // JSD: the chunk's teacher logits (pitch s_pitch) or null
   const float2 *stats_t;  // JSD: the teacher's block statistics or null
   const float *label_logit;  // global [BT]: fp32 S[r, y_r] from the logits GEMM, or null
+  const float *old_logprobs; // ratio heads: global [BT] old log-probs of the labels
+  float clip_low, clip_high; // ratio heads: the ratio is clipped to [1 - low, 1 + high]
 };
 void launch_row(const RowArgs &a, hipStream_t st);
 

@@ -28,6 +28,8 @@ constexpr int HEAD_KL = 0;
 constexpr int HEAD_SEL = 1;
 constexpr int HEAD_CE = 2;  // the selective head with the opposite sign
 constexpr int HEAD_JSD = 3;
+constexpr int HEAD_PPO = 4;    // clipped surrogate on the selective log-prob
+constexpr int HEAD_CISPO = 5;  // clipped ratio as a gradient-free weight
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -169,6 +171,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   const int64_t gr = a.row0 + lr;
   const int64_t V = a.V;
   char *rowp = reinterpret_cast<char *>(a.S) + lr * a.s_pitch * (SB ? 2 : 4);
+  static_assert(HEAD != HEAD_JSD, "the JSD head has its own row kernel");
   float *Srow = reinterpret_cast<float *>(rowp);                 // fp32 logits / dZ
   unsigned short *Zb = reinterpret_cast<unsigned short *>(rowp);  // bf16 dZ
   SRow<SB> sr{reinterpret_cast<decltype(SRow<SB>::p)>(rowp)};
@@ -219,7 +222,9 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
         for (int i = 0; i < 4; ++i) {
           if (e + i < V) {
             sq += t.v[i];
-            sqlogq += t.v[i] * __logf(fmaxf(t.v[i], a.eps));
+            // q = 0 adds exactly 0 whatever eps is [FusedLinearKLDivLoss
+            // page, Details: 0 log 0 contributes 0]
+            sqlogq += t.v[i] > 0.0f ? t.v[i] * __logf(fmaxf(t.v[i], a.eps)) : 0.0f;
           }
         }
       }
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
           if (e + i < V) {
             const float qi = t.v[i];
             sq += qi;
-            sqlogq += qi * __logf(fmaxf(qi, a.eps));
+            sqlogq += qi > 0.0f ? qi * __logf(fmaxf(qi, a.eps)) : 0.0f;
             sqx += qi * x.v[i];
           }
         }
@@ -292,6 +297,28 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     if (HEAD == HEAD_SEL) a.rowval[gr] = s_label - l;            // log p(y)
     if (HEAD == HEAD_CE) a.rowval[gr] = l - s_label;             // -log p(y)
     if (HEAD == HEAD_KL && !a.stats) a.rowval[gr] = A - B + Q * l;  // sum_v q log q - q (S - l)
+    if (HEAD == HEAD_PPO || HEAD == HEAD_CISPO) {
+      // rho = p(y) / p_old(y), c = clip(rho, 1 - low, 1 + high); the row's
+      // term L and k = dL / d log p(y) [frozen lm_head GRPO page, Summary:
+      // the GRPO family on the selective log-prob]
+      const float adv = a.weights ? a.weights[gr] : 1.0f;
+      const float lp = s_label - l;
+      const float rho = expf(lp - a.old_logprobs[gr]);
+      const float c = fminf(fmaxf(rho, 1.0f - a.clip_low), 1.0f + a.clip_high);
+      float L, k;
+      if (HEAD == HEAD_PPO) {
+        // -min(rho A, c A); the unclipped product takes ties and carries the
+        // gradient -rho A, the clipped one is constant in log p(y)
+        const float u = rho * adv, cl = c * adv;
+        L = -fminf(u, cl);
+        k = u <= cl ? -u : 0.0f;
+      } else {
+        L = -c * adv * lp;  // CISPO: c is a weight with no gradient
+        k = -c * adv;
+      }
+      a.rowval[gr] = L;
+      bcast[3] = k;
+    }
     bcast[0] = l;
     bcast[1] = Q;
     bcast[2] = A;
@@ -304,6 +331,8 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
   if (HEAD == HEAD_KL) {
     coef = g * a.inv_tau;
     Qr = bcast[1];
+  } else if (HEAD == HEAD_PPO || HEAD == HEAD_CISPO) {
+    coef = g * bcast[3] * a.inv_tau;  // dS = g k (onehot - p)
   } else {
     // selective: dS = g w (onehot - p); cross-entropy: dS = g w (p - onehot)
     const float w = a.weights ? a.weights[gr] : 1.0f;
@@ -737,6 +766,11 @@ void launch_row_t(const RowArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((row_kernel<HEAD_CE, SB>), dim3(a.rows), dim3(kRowThreads), 0, st, a);
   else if (a.head == HEAD_JSD)
     hipLaunchKernelGGL(jsd_row_kernel<SB>, dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else if (a.head == HEAD_PPO)
+    hipLaunchKernelGGL((row_kernel<HEAD_PPO, SB>), dim3(a.rows), dim3(kRowThreads), 0, st, a);
+  else if (a.head == HEAD_CISPO)
+    hipLaunchKernelGGL((row_kernel<HEAD_CISPO, SB>), dim3(a.rows), dim3(kRowThreads), 0, st,
+                       a);
 }
 
 void launch_row(const RowArgs &a, hipStream_t st) {

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(fll.LIB_PATH)
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert fll.fll_version() == 3
+    ver = int(re.search(r"#define FLL_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert fll.fll_version() == ver == fll.ABI_VERSION
     out = subprocess.run(["nm", "-D", "--defined-only", fll.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fll_\w+)", out))
@@ -51,9 +52,10 @@ def test_struct_layouts_match_the_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu %zu\\n", sizeof(fll_problem), sizeof(fll_plan_t), sizeof(fll_args),
          sizeof(fll_profile_t));
-  printf("%zu %zu %zu %zu\\n", offsetof(fll_problem, ignore_index),
+  printf("%zu %zu %zu %zu %zu %zu\\n", offsetof(fll_problem, ignore_index),
          offsetof(fll_plan_t, workspace_bytes), offsetof(fll_args, workspace_bytes),
-         offsetof(fll_profile_t, total_ms));
+         offsetof(fll_profile_t, total_ms), offsetof(fll_problem, clip_high),
+         offsetof(fll_args, old_logprobs));
   return 0;
 }}
 """)
@@ -66,7 +68,8 @@ int main(void) {{
     assert sizes == [ctypes.sizeof(fll.FllProblem), ctypes.sizeof(fll.FllPlan),
                      ctypes.sizeof(fll.FllArgs), ctypes.sizeof(fll.FllProfile)]
     assert offs == [fll.FllProblem.ignore_index.offset, fll.FllPlan.workspace_bytes.offset,
-                    fll.FllArgs.workspace_bytes.offset, fll.FllProfile.total_ms.offset]
+                    fll.FllArgs.workspace_bytes.offset, fll.FllProfile.total_ms.offset,
+                    fll.FllProblem.clip_high.offset, fll.FllArgs.old_logprobs.offset]
 
 
 # --------------------------------------------------------------------------
@@ -163,6 +166,13 @@ def test_plan_empty_batch():
     (dict(teacher_has_bias=True), fll.FLL_ERR_INVALID_ARG),
     (dict(logits_bf16=2), fll.FLL_ERR_INVALID_ARG),
     (dict(logits_bf16=True, dtype="fp32"), fll.FLL_ERR_INVALID_ARG),  # bf16 problems only
+    (dict(head="ppo", clip_low=-0.1), fll.FLL_ERR_INVALID_ARG),
+    (dict(head="ppo", clip_low=1.5), fll.FLL_ERR_INVALID_ARG),
+    (dict(head="ppo", clip_low=float("nan")), fll.FLL_ERR_INVALID_ARG),
+    (dict(head="cispo", clip_high=-1.0), fll.FLL_ERR_INVALID_ARG),
+    (dict(head="cispo", clip_high=float("nan")), fll.FLL_ERR_INVALID_ARG),
+    (dict(clip_low=0.2), fll.FLL_ERR_INVALID_ARG),                # clip for another head
+    (dict(head="kl", clip_high=0.2), fll.FLL_ERR_INVALID_ARG),
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(fll.FllError) as e:
@@ -246,6 +256,33 @@ def test_fwd_bwd_rejects_jsd(over, status):
                 b_teacher=14 * A)
     base.update(over)
     assert _call(plan, _args(plan, **base)) == status
+
+
+def test_plan_accepts_ratio_heads_without_upper_clip():
+    for head in ("ppo", "cispo"):
+        a = fll.fll_plan(_prob(head=head, clip_low=1.0, clip_high=float("inf")))
+        c = fll.fll_plan(_prob(head="selective"))
+        assert a.chunk_rows == c.chunk_rows and a.workspace_bytes == c.workspace_bytes
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(old_logprobs=None), fll.FLL_ERR_INVALID_ARG),
+    (dict(old_logprobs=15 * A + 2), fll.FLL_ERR_INVALID_ARG),
+    (dict(labels=None), fll.FLL_ERR_INVALID_ARG),
+    (dict(target=8 * A), fll.FLL_ERR_INVALID_ARG),
+    (dict(X_teacher=12 * A), fll.FLL_ERR_INVALID_ARG),
+])
+@pytest.mark.parametrize("head", ["ppo", "cispo"])
+def test_fwd_bwd_rejects_ratio(over, status, head):
+    plan = fll.fll_plan(_prob(BT=512, H=64, V=1000, head=head, clip_high=0.28))
+    base = dict(old_logprobs=15 * A)
+    base.update(over)
+    assert _call(plan, _args(plan, **base)) == status
+
+
+def test_fwd_bwd_rejects_old_logprobs_for_other_heads():
+    plan = fll.fll_plan(_prob(BT=512, H=64, V=1000))
+    assert _call(plan, _args(plan, old_logprobs=15 * A)) == fll.FLL_ERR_INVALID_ARG
 
 
 def test_fwd_bwd_rejects_teacher_inputs_for_other_heads():

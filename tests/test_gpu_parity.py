@@ -61,6 +61,24 @@ SMALL = {
     "kl-fp32-sum-ignored": workloads.small_case(
         BT=100, H=40, V=515, dtype="fp32", head="kl", reduction="sum", ignore_frac=0.2,
         compute_dW=True, x_std=1.0, w_std=0.1, temperature=0.75, seed=16),
+    # ratio heads (old log-probs = the oracle's log p(y) minus drawn
+    # log-ratios, kept off the clip edges): DAPO's wider upper clip, both
+    # clip branches, ragged shapes
+    "ppo-bf16-ragged-trainable-bias": workloads.small_case(
+        BT=300, H=264, V=1000, dtype="bf16", head="ppo", has_bias=True, compute_dW=True,
+        compute_db=True, clip_low=0.2, clip_high=0.28, logratio_std=0.4, temperature=2.0,
+        ignore_frac=0.1, reduction="mean", w_std=0.05, seed=41),
+    "cispo-bf16-odd-vocab-sum": workloads.small_case(
+        BT=520, H=136, V=777, dtype="bf16", head="cispo", compute_dW=True,
+        clip_low=0.2, clip_high=0.28, logratio_std=0.4, reduction="sum", ignore_frac=0.05,
+        w_std=0.05, seed=42),
+    "ppo-fp32-trainable": workloads.small_case(
+        BT=130, H=72, V=333, dtype="fp32", head="ppo", has_bias=True, compute_dW=True,
+        compute_db=True, clip_low=0.1, clip_high=0.1, logratio_std=0.3, x_std=1.0,
+        w_std=0.1, seed=43),
+    "ppo-bf16-no-clip-two-vocab-chunks": workloads.small_case(
+        BT=257, H=64, V=4099, dtype="bf16", head="ppo", clip_low=1.0,
+        clip_high=float("inf"), logratio_std=0.5, reduction="mean", w_std=0.05, seed=44),
 }
 
 
@@ -86,7 +104,7 @@ def test_small_parity_bf16_logits(name):
     case = SMALL[name]
     print(f"[parity bf16 logits] {name} {case}", flush=True)
     inp = H.make(case)
-    extra = 0.0 if case.head in ("selective", "ce") else H.logit_rounding_bound(inp, case)
+    extra = 0.0 if case.head in workloads.LABEL_HEADS else H.logit_rounding_bound(inp, case)
     H.compare_full(H.run_gpu(inp, case, logits_bf16=True), H.run_oracle(inp, case), case,
                    per_row_atol=extra)
 
@@ -102,6 +120,63 @@ def test_bf16_logits_dx_independent_of_gradient_flags(head):
     b = H.run_gpu(inp, case.replace(compute_dW=True, compute_db=True), logits_bf16=True)
     assert torch.equal(a["dX"], b["dX"])
     assert torch.equal(a["loss"], b["loss"])
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-10])
+def test_kl_one_hot_targets(eps):
+    # exact zeros in every target row: each contributes 0 to the KL (for
+    # eps = 0 too), which is then the cross-entropy (FusedLinearKLDivLoss
+    # page, Details: 0 log 0 contributes 0)
+    case = workloads.small_case(BT=300, H=264, V=1000, dtype="bf16", head="kl",
+                                has_bias=True, compute_dW=True, compute_db=True,
+                                temperature=2.0, ignore_frac=0.1, w_std=0.05, eps=eps,
+                                seed=45)
+    inp = H.make(case)
+    keep = inp["labels"] != case.ignore_index
+    q = torch.zeros_like(inp["target"])
+    q[keep, inp["labels"][keep]] = 1.0
+    q[~keep] = float("nan")
+    inp["target"] = q
+    out = H.run_gpu(inp, case)
+    assert torch.isfinite(out["per_row"]).all() and torch.isfinite(out["loss"])
+    H.compare_full(out, H.run_oracle(inp, case), case)
+    ce = H.run_gpu(dict(inp, target=None), case.replace(head="ce", with_weights=False))
+    torch.testing.assert_close(out["per_row"], ce["per_row"], rtol=2e-3, atol=2e-3)
+
+
+def test_ratio_clip_branches_on_the_gpu():
+    # the rows the oracle takes as clipped get exactly zero dlogits (dX row
+    # 0), the others not: the clip decision is the oracle's on every row
+    case = SMALL["ppo-bf16-ragged-trainable-bias"]
+    inp = H.make(case)
+    out = H.run_gpu(inp, case)
+    d = inp["logratio"].double()
+    old = H.ratio_old_logprobs(inp, case)
+    keep = inp["labels"] != case.ignore_index
+    A = inp["weights"].double()
+    rho = d.exp()
+    c = rho.clamp(1 - case.clip_low, 1 + case.clip_high)
+    clipped = keep & (rho * A > c * A)
+    assert 0 < int(clipped.sum()) < int(keep.sum())
+    zero_rows = (out["dX"].cpu() == 0).all(dim=1)
+    assert torch.equal(zero_rows, clipped | ~keep), (zero_rows ^ (clipped | ~keep)).nonzero()
+    assert torch.isfinite(old[keep]).all()
+
+
+@pytest.mark.parametrize("head", ["ppo", "cispo"])
+def test_ratio_heads_at_ratio_one_match_the_selective_head(head):
+    # old = the oracle's log p(y): every ratio is one (up to fp32 rounding of
+    # the input), so dX equals the selective head's with weights -A
+    case = SMALL["ppo-bf16-ragged-trainable-bias"].replace(head=head)
+    inp = H.make(case)
+    inp["logratio"] = torch.zeros_like(inp["logratio"])
+    out = H.run_gpu(inp, case)
+    sel_case = case.replace(head="selective")
+    sel_inp = dict(inp, weights=-inp["weights"])
+    sel = H.run_gpu(sel_inp, sel_case)
+    torch.testing.assert_close(out["dX"].float(), sel["dX"].float(), rtol=2e-2,
+                               atol=1e-2 * float(sel["dX"].float().abs().max()))
+    H.check_grad(out["dW"].cpu().numpy(), sel["dW"].cpu().numpy(), "bf16", "dW vs selective")
 
 
 def test_unnormalised_target():
