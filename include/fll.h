@@ -250,6 +250,25 @@ int fll_plan(const fll_problem *problem, size_t max_workspace_bytes,
  * FLL_ERR_WORKSPACE, or FLL_ERR_HIP (launch failure; see fll_last_error). */
 int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as fll_fwd_bwd, with the workspace taken from a fixed array that the
+ * library keeps on each device it runs on (FLL_STATIC_SCRATCH_BYTES, held
+ * from the first call on a device until the process ends) instead of the
+ * caller's. It allocates nothing and records no profiling events.
+ *
+ *   plan    from fll_plan(problem, FLL_STATIC_SCRATCH_BYTES, ..., &plan), so
+ *           the chunk size fits the array; a plan needing more workspace is
+ *           refused with FLL_ERR_WORKSPACE.
+ *   args    as for fll_fwd_bwd, but workspace must be NULL and
+ *           workspace_bytes 0 (else FLL_ERR_INVALID_ARG).
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (other streams, other threads) race and must be ordered by
+ * the caller. Nothing in the array needs clearing between calls. Returns the
+ * codes of fll_fwd_bwd. */
+#define FLL_STATIC_SCRATCH_BYTES ((size_t)512 << 20)
+int fll_fwd_bwd_static(const fll_plan_t *plan, const fll_args *args, fll_stream stream);
+
 /* Static text for a status code. */
 const char *fll_strerror(int status);
 

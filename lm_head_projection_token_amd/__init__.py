@@ -117,6 +117,9 @@ def _load():
     lib.fll_fwd_bwd.argtypes = [ctypes.POINTER(FllPlan), ctypes.POINTER(FllArgs),
                                 ctypes.c_void_p]
     lib.fll_fwd_bwd.restype = ctypes.c_int
+    lib.fll_fwd_bwd_static.argtypes = [ctypes.POINTER(FllPlan), ctypes.POINTER(FllArgs),
+                                       ctypes.c_void_p]
+    lib.fll_fwd_bwd_static.restype = ctypes.c_int
     lib.fll_strerror.argtypes = [ctypes.c_int]
     lib.fll_strerror.restype = ctypes.c_char_p
     lib.fll_last_error.argtypes = []
@@ -136,8 +139,11 @@ def _load():
 _lib = _load()
 
 # Symbols declared in include/fll.h (checked by the CPU tests).
-EXPORTS = ("fll_plan", "fll_fwd_bwd", "fll_strerror", "fll_last_error", "fll_version",
-           "fll_profile_enable", "fll_profile_read")
+EXPORTS = ("fll_plan", "fll_fwd_bwd", "fll_fwd_bwd_static", "fll_strerror",
+           "fll_last_error", "fll_version", "fll_profile_enable", "fll_profile_read")
+
+# bytes of the library's per-device scratch used by fll_fwd_bwd_static
+FLL_STATIC_SCRATCH_BYTES = 512 << 20
 
 
 def lib():
@@ -231,6 +237,37 @@ def fll_fwd_bwd(plan: FllPlan, *, X, W, b=None, labels=None, target=None, weight
     else:
         handle = stream.cuda_stream
     _check(_lib.fll_fwd_bwd(ctypes.byref(plan), ctypes.byref(args), ctypes.c_void_p(handle)))
+
+
+def fll_fwd_bwd_static(plan: FllPlan, *, X, W, b=None, labels=None, target=None,
+                       weights=None, dX, dW=None, db=None, loss, per_row=None, stream=None,
+                       X_teacher=None, W_teacher=None, b_teacher=None,
+                       old_logprobs=None) -> None:
+    """``fll_fwd_bwd`` with the library's static per-device scratch as the
+    workspace (plan with ``max_workspace_bytes=FLL_STATIC_SCRATCH_BYTES``):
+    allocates nothing. Calls that overlap on one device race."""
+    import torch
+
+    for name, t in (("X", X), ("W", W), ("b", b), ("labels", labels), ("target", target),
+                    ("weights", weights), ("dX", dX), ("dW", dW), ("db", db),
+                    ("loss", loss), ("per_row", per_row), ("X_teacher", X_teacher),
+                    ("W_teacher", W_teacher), ("b_teacher", b_teacher),
+                    ("old_logprobs", old_logprobs)):
+        if isinstance(t, torch.Tensor) and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    args = FllArgs(X=_ptr(X), W=_ptr(W), b=_ptr(b), labels=_ptr(labels),
+                   target=_ptr(target), weights=_ptr(weights), dX=_ptr(dX), dW=_ptr(dW),
+                   db=_ptr(db), loss=_ptr(loss), per_row=_ptr(per_row), workspace=None,
+                   workspace_bytes=0, X_teacher=_ptr(X_teacher), W_teacher=_ptr(W_teacher),
+                   b_teacher=_ptr(b_teacher), old_logprobs=_ptr(old_logprobs))
+    if stream is None:
+        handle = torch.cuda.current_stream().cuda_stream
+    elif isinstance(stream, int):
+        handle = stream
+    else:
+        handle = stream.cuda_stream
+    _check(_lib.fll_fwd_bwd_static(ctypes.byref(plan), ctypes.byref(args),
+                                   ctypes.c_void_p(handle)))
 
 
 def fll_profile_enable(enable: bool = True) -> None:

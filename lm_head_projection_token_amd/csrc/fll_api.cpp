@@ -274,8 +274,8 @@ struct Probe {
   int kind;
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
-  Probe(int k, hipStream_t s) : kind(k), st(s) {
-    if (!g_prof_on) return;
+  Probe(int k, hipStream_t s, bool timed) : kind(k), st(s) {
+    if (!timed || !g_prof_on) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     a = pooled_event();
     b = pooled_event();
@@ -289,6 +289,37 @@ struct Probe {
   }
 };
 
+// ---- the allocation-free entry point's scratch --------------------------
+// One array per device, in the library's device code; its address on a
+// device comes from hipGetSymbolAddress, once per device (the array's name
+// in host code is only a host-side handle, not a device address). Every
+// fll_fwd_bwd_static call on a device shares it, so overlapping calls on one
+// device race; the call writes every region it reads before reading it, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) char scratch[FLL_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FLL_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FLL_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FLL_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLL_OK;
+}
+
 int hip_check(const char *what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
@@ -296,36 +327,10 @@ int hip_check(const char *what) {
   return FLL_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fll_version(void) { return FLL_VERSION; }
-
-const char *fll_strerror(int status) {
-  switch (status) {
-    case FLL_OK: return "ok";
-    case FLL_ERR_INVALID_ARG: return "invalid argument";
-    case FLL_ERR_UNSUPPORTED: return "unsupported request";
-    case FLL_ERR_WORKSPACE: return "workspace missing, too small or over budget";
-    case FLL_ERR_HIP: return "HIP error";
-    default: return "unknown status";
-  }
-}
-
-const char *fll_last_error(void) { return g_err; }
-
-int fll_plan(const fll_problem *problem, size_t max_workspace_bytes, int64_t chunk_rows,
-             fll_plan_t *plan) {
-  g_err[0] = 0;
-  return make_plan(problem, max_workspace_bytes, chunk_rows, plan);
-}
-
-int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream) {
-  g_err[0] = 0;
-  int st = check_args(plan, args);
-  if (st) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+// Enqueue one checked call: the per-chunk kernel sequence over the
+// workspace args->workspace. timed: record the profiling events (when on).
+int enqueue(const fll_plan_t *plan, const fll_args *args, hipStream_t s, bool timed) {
+  int st = FLL_OK;
   // hipGetLastError reports the last failure of any HIP caller on this
   // thread; drop a stale one left by another library so only this call's
   // launches are judged below.
@@ -358,7 +363,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
   }
 
   {
-    Probe pr(FLL_K_PREP, s);
+    Probe pr(FLL_K_PREP, s, timed);
     fll::launch_prep(a.labels, p.BT, p.ignore_index, p.head, p.reduction, p.V, sc, s);
   }
   if ((st = hip_check("prep"))) return st;
@@ -373,7 +378,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       // the teacher's own projection: T = (X_t W_t^T + b_t) / tau, with its
       // row statistics [FusedLinearKLDivLoss page, Summary]
       const char *Xtc = static_cast<const char *>(a.X_teacher) + size_t(r0) * p.H_teacher * esz;
-      Probe pr(FLL_K_TEACHER, s);
+      Probe pr(FLL_K_TEACHER, s, timed);
       if (bf16)
         fll::launch_logits_bf16(Xtc, p.H_teacher, a.W_teacher, p.H_teacher, a.b_teacher,
                                 inv_tau, T, plan->s_pitch, p.logits_bf16, stats_t,
@@ -387,7 +392,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     }
     if ((st = hip_check("teacher logits GEMM"))) return st;
     {
-      Probe pr(FLL_K_LOGITS, s);
+      Probe pr(FLL_K_LOGITS, s, timed);
       if (bf16)
         fll::launch_logits_bf16(Xc, p.H, a.W, p.H, a.b, inv_tau, S, plan->s_pitch,
                                 p.logits_bf16, stats, plan->stat_tiles, rows, p.V, p.H,
@@ -425,7 +430,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       ra.old_logprobs = a.old_logprobs;
       ra.clip_low = p.clip_low;
       ra.clip_high = p.clip_high;
-      Probe pr(FLL_K_ROW, s);
+      Probe pr(FLL_K_ROW, s, timed);
       fll::launch_row(ra, s);
     }
     if ((st = hip_check("row kernel"))) return st;
@@ -434,7 +439,7 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     // in place (pitch s_pitch).
     const int64_t ldz = bf16 && !p.logits_bf16 ? 2 * plan->s_pitch : plan->s_pitch;
     {
-      Probe pr(FLL_K_DX, s);
+      Probe pr(FLL_K_DX, s, timed);
       if (bf16)
         fll::launch_dx_bf16(S, ldz, a.W, p.H, dXc, p.H, partial, rows, p.H, p.V,
                             plan->dx_splits, plan->dx_split_len, s);
@@ -445,12 +450,12 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
     }
     if ((st = hip_check("dX GEMM"))) return st;
     if (plan->dx_splits > 1) {
-      Probe pr(FLL_K_DX_REDUCE, s);
+      Probe pr(FLL_K_DX_REDUCE, s, timed);
       fll::launch_dx_reduce(partial, plan->dx_splits, rows, p.H, dXc, p.H, bf16 ? 1 : 0, s);
       if ((st = hip_check("dX reduce"))) return st;
     }
     if (p.compute_dW) {
-      Probe pr(FLL_K_DW, s);
+      Probe pr(FLL_K_DW, s, timed);
       if (bf16)
         fll::launch_dw_bf16(S, ldz, Xc, p.H, a.dW, p.V, p.H, rows, c > 0, s);
       else
@@ -459,18 +464,73 @@ int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream)
       if ((st = hip_check("dW GEMM"))) return st;
     }
     if (p.compute_db) {
-      Probe pr(FLL_K_DB, s);
+      Probe pr(FLL_K_DB, s, timed);
       fll::launch_colsum(S, bf16 ? 1 : 0, ldz, rows, p.V, partial, a.db, c > 0, s);
       if ((st = hip_check("db column sums"))) return st;
     }
   }
   {
-    Probe pr(FLL_K_FINAL, s);
+    Probe pr(FLL_K_FINAL, s, timed);
     // the ratio heads' advantages are inside their per-row terms already
     const bool weighted = p.head == FLL_HEAD_SELECTIVE_LOGPROB || p.head == FLL_HEAD_CROSS_ENTROPY;
     fll::launch_finalize(rowval, weighted ? a.weights : nullptr, p.BT, sc, a.loss, s);
   }
   return hip_check("loss reduction");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fll_version(void) { return FLL_VERSION; }
+
+const char *fll_strerror(int status) {
+  switch (status) {
+    case FLL_OK: return "ok";
+    case FLL_ERR_INVALID_ARG: return "invalid argument";
+    case FLL_ERR_UNSUPPORTED: return "unsupported request";
+    case FLL_ERR_WORKSPACE: return "workspace missing, too small or over budget";
+    case FLL_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *fll_last_error(void) { return g_err; }
+
+int fll_fwd_bwd(const fll_plan_t *plan, const fll_args *args, fll_stream stream) {
+  g_err[0] = 0;
+  int st = check_args(plan, args);
+  if (st) return st;
+  return enqueue(plan, args, reinterpret_cast<hipStream_t>(stream), true);
+}
+
+int fll_fwd_bwd_static(const fll_plan_t *plan, const fll_args *args, fll_stream stream) {
+  g_err[0] = 0;
+  if (!plan || !args) return fail(FLL_ERR_INVALID_ARG, "plan or args is NULL");
+  if (args->workspace || args->workspace_bytes)
+    return fail(FLL_ERR_INVALID_ARG,
+                "fll_fwd_bwd_static uses the library's scratch: workspace must be NULL "
+                "and workspace_bytes 0");
+  if (plan->workspace_bytes > FLL_STATIC_SCRATCH_BYTES)
+    return fail(FLL_ERR_WORKSPACE,
+                "the plan needs %zu workspace bytes, more than the %zu of the static "
+                "scratch: plan with max_workspace_bytes = FLL_STATIC_SCRATCH_BYTES",
+                plan->workspace_bytes, size_t(FLL_STATIC_SCRATCH_BYTES));
+  void *ptr = nullptr;
+  int st = scratch_on_current_device(&ptr);
+  if (st) return st;
+  fll_args a = *args;
+  a.workspace = ptr;
+  a.workspace_bytes = FLL_STATIC_SCRATCH_BYTES;
+  st = check_args(plan, &a);
+  if (st) return st;
+  return enqueue(plan, &a, reinterpret_cast<hipStream_t>(stream), false);
+}
+
+int fll_plan(const fll_problem *problem, size_t max_workspace_bytes, int64_t chunk_rows,
+             fll_plan_t *plan) {
+  g_err[0] = 0;
+  return make_plan(problem, max_workspace_bytes, chunk_rows, plan);
 }
 
 int fll_profile_enable(int enable) {

@@ -52,6 +52,7 @@ def test_struct_layouts_match_the_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu %zu\\n", sizeof(fll_problem), sizeof(fll_plan_t), sizeof(fll_args),
          sizeof(fll_profile_t));
+  printf("%zu\\n", (size_t)FLL_STATIC_SCRATCH_BYTES);
   printf("%zu %zu %zu %zu %zu %zu\\n", offsetof(fll_problem, ignore_index),
          offsetof(fll_plan_t, workspace_bytes), offsetof(fll_args, workspace_bytes),
          offsetof(fll_profile_t, total_ms), offsetof(fll_problem, clip_high),
@@ -64,7 +65,8 @@ int main(void) {{
     lines = subprocess.run([str(exe)], capture_output=True, text=True,
                            check=True).stdout.split("\n")
     sizes = [int(x) for x in lines[0].split()]
-    offs = [int(x) for x in lines[1].split()]
+    assert int(lines[1]) == fll.FLL_STATIC_SCRATCH_BYTES
+    offs = [int(x) for x in lines[2].split()]
     assert sizes == [ctypes.sizeof(fll.FllProblem), ctypes.sizeof(fll.FllPlan),
                      ctypes.sizeof(fll.FllArgs), ctypes.sizeof(fll.FllProfile)]
     assert offs == [fll.FllProblem.ignore_index.offset, fll.FllPlan.workspace_bytes.offset,
@@ -325,6 +327,36 @@ def test_fwd_bwd_rejects_edited_plan():
     plan = fll.fll_plan(_prob(BT=512, H=64, V=1000))
     plan.p.reduction = fll.FLL_RED_NONE
     assert _call(plan, _args(plan)) == fll.FLL_ERR_UNSUPPORTED
+
+
+def test_static_entry_point_refusals_before_any_device_call():
+    # the scratch-backed call checks its own arguments on the host first
+    lib = fll.lib()
+    small = fll.fll_plan(_prob(BT=512, H=64, V=1000), fll.FLL_STATIC_SCRATCH_BYTES)
+    assert small.workspace_bytes <= fll.FLL_STATIC_SCRATCH_BYTES
+    # a caller workspace is refused: the call uses the library's own
+    args = _args(small)
+    assert lib.fll_fwd_bwd_static(ctypes.byref(small), ctypes.byref(args),
+                                  None) == fll.FLL_ERR_INVALID_ARG
+    assert "workspace must be NULL" in fll.fll_last_error()
+    # a plan made for a larger budget does not fit the scratch
+    big = fll.fll_plan(_prob())
+    assert big.workspace_bytes > fll.FLL_STATIC_SCRATCH_BYTES
+    args = _args(big, workspace=None, workspace_bytes=0)
+    assert lib.fll_fwd_bwd_static(ctypes.byref(big), ctypes.byref(args),
+                                  None) == fll.FLL_ERR_WORKSPACE
+    assert "FLL_STATIC_SCRATCH_BYTES" in fll.fll_last_error()
+    assert lib.fll_fwd_bwd_static(None, ctypes.byref(args), None) == fll.FLL_ERR_INVALID_ARG
+
+
+def test_static_scratch_budget_plans_the_head_shapes():
+    # the 512 MiB scratch fits every named head shape at a reduced chunk
+    for kw in (dict(), dict(V=151936, has_bias=True, compute_dW=True, compute_db=True),
+               dict(head="kl", BT=4096, compute_dW=True),
+               dict(head="jsd", BT=4096, H_teacher=4096)):
+        plan = fll.fll_plan(_prob(**kw), fll.FLL_STATIC_SCRATCH_BYTES)
+        assert plan.workspace_bytes <= fll.FLL_STATIC_SCRATCH_BYTES
+        assert plan.chunk_rows >= 256
 
 
 def test_fwd_bwd_rejects_null_plan_and_args():
