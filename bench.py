@@ -9,7 +9,10 @@ Default workload: GRPO selective log-prob with a frozen head, B=8, T=1024
 (BT = 8192 tokens), H = 4096, V = 128256, bf16 -- the head shape and batch
 the frozen lm_head GRPO page times (Details). ``--config 5`` selects the
 trainable KL distillation workload at the same H and V, ``--config jsd`` the
-Jensen-Shannon head against a teacher with its own H = 4096 projection.
+Jensen-Shannon head against a teacher with its own H = 4096 projection,
+``--config ppo`` the PPO clipped surrogate on the default workload's shape
+(its old log-probs are -log V minus the drawn log-ratios: the work per row
+does not depend on which clip branch a row takes).
 
 Prints one JSON line. ``value`` and ``ms_per_step`` come from the timed
 steps alone; ``kernels`` and ``roofline`` (the dominant kernel) from as many
@@ -24,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -56,6 +60,38 @@ def measured_traffic(case, kind, logits_bf16=False):
     if not k:
         return None
     return k["fetch_bytes"] + k["write_bytes"]
+
+
+def measured_clock(case, kind, logits_bf16=False):
+    """Shader clock (GHz) and MFMA busy fraction of `kind` from the committed
+    counter summary of this workload (GRBM_COUNT over the kernel's duration),
+    or None if there is none or the kernels changed since."""
+    from lm_head_projection_token_amd import profiling
+
+    tag = case.name + ("-bf16-logits" if logits_bf16 else "")
+    path = os.path.join(ROOT, "profiles", f"mfma_{tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("src_sha256") != profiling.source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kind)
+    if not k or not k.get("clock_GHz"):
+        return None
+    return k["clock_GHz"], k.get("mfma_busy")
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
 
 
 def gemm_flops(case):
@@ -137,8 +173,10 @@ def clock_record(clk, case, ms, achieved):
     """The clock object of the JSON line from sample_clock's readings. A
     reading whose peak at that clock is below what the dominant kernel was
     measured to reach cannot be the clock it ran at (amd-smi can report a
-    stale or idle value while short kernels run): the figures are then left
-    out and the record says why."""
+    stale or idle value while short kernels run), and readings that repeat
+    to the kHz are amd-smi's slowly refreshed figure, not the clock of the
+    steps: in both cases no fraction is derived from them and the record
+    says why (the per-kernel clock of ``roofline`` comes from counters)."""
     ghz = clk[0]
     peak_at_clock = (PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_FP32_TFLOPS) * ghz / 2.4
     rec = {"source": "amd-smi metric --clock (GFX clock averaged over the XCDs) while "
@@ -148,13 +186,17 @@ def clock_record(clk, case, ms, achieved):
         rec.update(GHz=None, discarded_GHz=ghz,
                    note="readings below the clock the measured throughput needs; discarded")
         return rec
+    if clk[3] > 1 and clk[1] == clk[2]:
+        rec["note"] = ("every reading identical: a stale amd-smi figure, so no fraction "
+                       "at this clock is given")
+        return rec
     rec.update(peak_at_clock=peak_at_clock,
                end_to_end_frac_at_clock=gemm_flops(case) / (ms / 1e3) / 1e12 / peak_at_clock,
                roofline_frac_at_clock=achieved / peak_at_clock)
     return rec
 
 
-def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
+def cpu_baseline(inp, case, rows_small=256, rows_big=3072, old=None):
     """Time the oracle on two row samples and extrapolate to the full batch."""
     import numpy as np
 
@@ -185,7 +227,9 @@ def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
             reduction=case.reduction, ignore_index=case.ignore_index,
             temperature=case.temperature, eps=case.eps,
             Xt_rows=None if inp["X_teacher"] is None else inp["X_teacher"][:R].double().numpy(),
-            W_teacher=Wt, b_teacher=bt)
+            W_teacher=Wt, b_teacher=bt,
+            old_logprobs_rows=None if old is None else old[:R].double().numpy(),
+            clip_low=case.clip_low, clip_high=case.clip_high)
         return time.perf_counter() - t0
 
     t1 = run(rows_small)
@@ -195,6 +239,7 @@ def cpu_baseline(inp, case, rows_small=256, rows_big=3072):
     est = fixed + per_row * case.BT
     return {
         "value": case.BT / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"numpy float64 oracle (sampled_rows: logits, log-softmax, loss terms, "
                    f"dlogits, dX{', teacher logits' if case.head == 'jsd' else ''}) timed on "
                    f"the first {rows_small} and {rows_big} token rows "
@@ -208,7 +253,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="3", choices=["2", "3", "4", "5", "jsd"])
+    ap.add_argument("--config", default="3", choices=["2", "3", "4", "5", "jsd", "ppo"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--logits-bf16", action="store_true",
@@ -241,8 +286,13 @@ def main():
     import lm_head_projection_token_amd as fll
     import workloads
 
-    case = workloads.JSD_WORKLOAD if args.config == "jsd" else workloads.WORKLOADS[int(args.config)]
+    named = {"jsd": workloads.JSD_WORKLOAD, "ppo": workloads.PPO_WORKLOAD}
+    case = named[args.config] if args.config in named else workloads.WORKLOADS[int(args.config)]
     inp = workloads.make_inputs(case)
+    old = None
+    if case.head in workloads.RATIO_HEADS:
+        # synthetic old log-probs: the time per row does not depend on them
+        old = -math.log(case.V) - inp["logratio"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -252,13 +302,16 @@ def main():
     X, W, b = d(inp["X"]), d(inp["W"]), d(inp["b"])
     labels, target, weights = d(inp["labels"]), d(inp["target"]), d(inp["weights"])
     Xt, Wt, bt = d(inp["X_teacher"]), d(inp["W_teacher"]), d(inp["b_teacher"])
+    old_d = d(old)
     prob = fll.make_problem(case.BT, case.H, case.V, dtype=case.dtype, head=case.head,
                             has_bias=case.has_bias, compute_dW=case.compute_dW,
                             compute_db=case.compute_db, reduction=case.reduction,
                             ignore_index=case.ignore_index, temperature=case.temperature,
                             eps=case.eps, H_teacher=case.H_teacher,
                             teacher_has_bias=case.teacher_has_bias,
-                            logits_bf16=args.logits_bf16)
+                            logits_bf16=args.logits_bf16,
+                            clip_low=case.clip_low if old is not None else None,
+                            clip_high=case.clip_high if old is not None else None)
     plan = fll.fll_plan(prob, 0, args.chunk_rows)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     dX = torch.empty_like(X)
@@ -270,7 +323,7 @@ def main():
     def step():
         fll.fll_fwd_bwd(plan, X=X, W=W, b=b, labels=labels, target=target, weights=weights,
                         dX=dX, dW=dW, db=db, loss=loss, workspace=ws, stream=stream,
-                        X_teacher=Xt, W_teacher=Wt, b_teacher=bt)
+                        X_teacher=Xt, W_teacher=Wt, b_teacher=bt, old_logprobs=old_d)
 
     for _ in range(args.warmup):
         step()
@@ -317,6 +370,12 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic(case, dom, args.logits_bf16),
                 "flops_per_launch": per_launch}
+    clk = measured_clock(case, dom, args.logits_bf16)
+    if clk:
+        # the clock this kernel ran at, from the committed counter summary
+        # (GRBM_COUNT over the kernel's duration) of the same kernel sources
+        roofline.update(counter_clock_GHz=clk[0], counter_mfma_busy=clk[1],
+                        frac_at_counter_clock=achieved / (peak * clk[0] / 2.4))
     row = kernels.get("row")
     if row:
         bytes_per_row = row_bytes_per_valid_row(case, args.logits_bf16)
@@ -350,7 +409,7 @@ def main():
             out["clock"] = clock_record(clk, case, ms, achieved)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, case)
+        out["cpu_baseline"] = cpu_baseline(inp, case, old=old)
     print(json.dumps(out))
 
 

@@ -21,7 +21,9 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfll.so")
+# FLL_LIBRARY names another build of the same library (the host-sanitized
+# one the CPU tests build); by default the in-tree libfll.so
+LIB_PATH = os.environ.get("FLL_LIBRARY") or os.path.join(PKG, "libfll.so")
 ABI_VERSION = 4  # FLL_VERSION of include/fll.h that the structs below mirror
 
 FLL_OK = 0

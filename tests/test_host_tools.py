@@ -213,6 +213,38 @@ def test_clock_record_discards_impossible_readings():
     assert "roofline_frac_at_clock" not in bad
 
 
+def test_clock_record_gives_no_fraction_for_identical_readings():
+    # readings that repeat to the kHz are a stale amd-smi figure
+    case = workloads.WORKLOADS[3]
+    stale = bench.clock_record((2.2295, 2.2295, 2.2295, 6), case, 13.0, 1300.0)
+    assert stale["GHz"] == 2.2295 and "stale" in stale["note"]
+    assert "roofline_frac_at_clock" not in stale and "end_to_end_frac_at_clock" not in stale
+    one = bench.clock_record((1.8, 1.8, 1.8, 1), case, 13.0, 1300.0)
+    assert "roofline_frac_at_clock" in one
+
+
+def test_measured_clock_needs_matching_sources(tmp_path, monkeypatch):
+    from lm_head_projection_token_amd import profiling
+
+    case = workloads.WORKLOADS[3]
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"src_sha256": profiling.source_hash(),
+           "kernels": {"logits": {"clock_GHz": 1.82, "mfma_busy": 0.69}}}
+    (prof / f"mfma_{case.name}.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_clock(case, "logits") == (1.82, 0.69)
+    assert bench.measured_clock(case, "dx") is None
+    rec["src_sha256"] = "0" * 64
+    (prof / f"mfma_{case.name}.json").write_text(json.dumps(rec))
+    assert bench.measured_clock(case, "logits") is None
+
+
+def test_cpu_model_is_named():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
+
+
 def test_lds_summary_per_cu_and_conflict_share(tmp_path):
     d = tmp_path / "l"
     d.mkdir()

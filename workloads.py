@@ -110,6 +110,13 @@ JSD_WORKLOAD = Case("jsd-distill-bf16-frozen-V128256", BT=4096, H=4096, V=128256
                     ignore_frac=0.1, seed=9)
 
 
+# The PPO clipped surrogate (DAPO's wider upper clip) on the frozen GRPO
+# workload's shape: B=8, T=1024, H=4096, V=128256, advantages ~ N(0, 1).
+PPO_WORKLOAD = Case("ppo-bf16-frozen-B8T1024-V128256", BT=8192, H=4096, V=128256,
+                    dtype="bf16", head=HEAD_PPO, reduction="mean", clip_low=0.2,
+                    clip_high=0.28, seed=7)
+
+
 def _normal(gen: torch.Generator, shape, std: float) -> torch.Tensor:
     t = torch.empty(shape, dtype=torch.float32)
     t.normal_(0.0, std, generator=gen)
