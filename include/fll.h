@@ -286,11 +286,12 @@ enum {
   FLL_K_ROW = 2,      /* fused row kernel (softmax, loss, dlogits)      */
   FLL_K_DX = 3,       /* dX GEMM                                        */
   FLL_K_DX_REDUCE = 4,/* dX split reduction                             */
-  FLL_K_DW = 5,       /* dW GEMM                                        */
-  FLL_K_DB = 6,       /* db column sums                                 */
+  FLL_K_DW = 5,       /* dW GEMM (bf16: with db when both are asked for)*/
+  FLL_K_DB = 6,       /* db column sums (db without dW, or fp32)        */
   FLL_K_FINAL = 7,    /* loss reduction                                 */
   FLL_K_TEACHER = 8,  /* JSD: teacher logits GEMM                       */
-  FLL_K_COUNT = 9
+  FLL_K_TRANSPOSE = 9,/* bf16 dW: the chunk's X transposed              */
+  FLL_K_COUNT = 10
 };
 
 typedef struct {

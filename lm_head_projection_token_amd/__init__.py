@@ -50,7 +50,7 @@ FLL_BF16, FLL_FP32 = 0, 1
 DTYPES = {"bf16": FLL_BF16, "fp32": FLL_FP32}
 
 KERNEL_KINDS = ["prep", "logits", "row", "dx", "dx_reduce", "dw", "db", "final",
-                "teacher"]
+                "teacher", "transpose"]
 
 
 class FllProblem(ctypes.Structure):
@@ -93,7 +93,8 @@ class FllArgs(ctypes.Structure):
 
 
 class FllProfile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 9), ("total_ms", ctypes.c_double * 9)]
+    _fields_ = [("launches", ctypes.c_int64 * len(KERNEL_KINDS)),
+                ("total_ms", ctypes.c_double * len(KERNEL_KINDS))]
 
 
 class FllError(RuntimeError):

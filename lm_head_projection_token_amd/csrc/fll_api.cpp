@@ -124,14 +124,16 @@ void layout(fll_plan_t *pl, int64_t C) {
   off = align256(off + size_t(std::max<int64_t>(p.BT, 1)) * 4);
   pl->off_stats = off;
   off = align256(off + size_t(C) * size_t(pl->stat_tiles) * 8);
-  // fp32 partial sums: of the dX splits, and (after dX is reduced) of the
-  // db column sums over kDbSplits row ranges; sized for both whatever the
-  // flags, so C does not depend on them
+  // fp32 partial sums of the dX splits; after dX is reduced the same bytes
+  // hold the db column sums over kDbSplits row ranges (db without dW) or the
+  // chunk's X transposed for the bf16 dW GEMM. Sized for all three whatever
+  // the flags, so C does not depend on them.
   pl->off_dx_partial = off;
   {
     const size_t dx_part = pl->dx_splits > 1 ? size_t(pl->dx_splits) * C * p.H * 4 : 0;
     const size_t db_part = size_t(fll::kDbSplits) * size_t(p.V) * 4;
-    off = align256(off + std::max(dx_part, db_part));
+    const size_t xt_part = p.dtype == FLL_BF16 ? size_t(p.H) * size_t(rup(C, 64)) * 2 : 0;
+    off = align256(off + std::max(std::max(dx_part, db_part), xt_part));
   }
   pl->off_scalars = off;
   off = align256(off + sizeof(fll::DevScalars));
@@ -454,16 +456,27 @@ int enqueue(const fll_plan_t *plan, const fll_args *args, hipStream_t s, bool ti
       fll::launch_dx_reduce(partial, plan->dx_splits, rows, p.H, dXc, p.H, bf16 ? 1 : 0, s);
       if ((st = hip_check("dX reduce"))) return st;
     }
+    // bf16: db is formed inside the dW GEMM when both are asked for
+    const bool db_in_dw = bf16 && p.compute_dW && p.compute_db;
+    if (p.compute_dW && bf16) {
+      // the chunk's X transposed (H x C, pitch a multiple of 64 tokens), so
+      // that the dW GEMM reads both operands along its token dimension in
+      // whole cache lines; the dX partials are reduced by now
+      Probe pr(FLL_K_TRANSPOSE, s, timed);
+      fll::launch_transpose_bf16(Xc, p.H, rows, p.H, partial, rup(C, 64), s);
+      if ((st = hip_check("X transpose"))) return st;
+    }
     if (p.compute_dW) {
       Probe pr(FLL_K_DW, s, timed);
       if (bf16)
-        fll::launch_dw_bf16(S, ldz, Xc, p.H, a.dW, p.V, p.H, rows, c > 0, s);
+        fll::launch_dw_bf16(S, ldz, partial, rup(C, 64), a.dW, db_in_dw ? a.db : nullptr, p.V,
+                            p.H, rows, c > 0, s);
       else
         fll::launch_dw_f32(S, ldz, reinterpret_cast<const float *>(Xc), p.H, a.dW,
                            p.V, p.H, rows, c > 0, s);
       if ((st = hip_check("dW GEMM"))) return st;
     }
-    if (p.compute_db) {
+    if (p.compute_db && !db_in_dw) {
       Probe pr(FLL_K_DB, s, timed);
       fll::launch_colsum(S, bf16 ? 1 : 0, ldz, rows, p.V, partial, a.db, c > 0, s);
       if ((st = hip_check("db column sums"))) return st;

@@ -40,11 +40,17 @@ void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw,
                     void *dX, int64_t ldo, float *partial, int64_t M, int64_t N,
                     int64_t K, int64_t splits, int64_t split_len, hipStream_t st);
 
-// dW[m, n] (+)= sum_k dZ[k, m] X[k, n]: dZ bf16 [K x M] pitch ldz,
-// X [K x N] pitch ldx, dW fp32 [M x N] pitch N. accumulate = 0 stores.
-void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx,
-                    float *dW, int64_t M, int64_t N, int64_t K, int accumulate,
-                    hipStream_t st);
+// dW[m, n] (+)= sum_k dZ[k, m] X[k, n]: dZ bf16 [K x M] pitch ldz, the
+// chunk's X transposed, XT bf16 [N x K] pitch ldxt (16-byte aligned rows),
+// dW fp32 [M x N] pitch N. accumulate = 0 stores.
+// db (or null): db[m] (+)= sum_k dZ[k, m] for m < M, in the same launch.
+void launch_dw_bf16(const void *dZ, int64_t ldz, const void *XT, int64_t ldxt,
+                    float *dW, float *db, int64_t M, int64_t N, int64_t K,
+                    int accumulate, hipStream_t st);
+
+// XT[c, r] = X[r, c] for r < rows, c < cols (bf16): X pitch ldx, XT pitch ldt.
+void launch_transpose_bf16(const void *X, int64_t ldx, int64_t rows, int64_t cols, void *XT,
+                           int64_t ldt, hipStream_t st);
 
 // ---- fp32 MFMA GEMMs (gemm_fp32.hip), same contracts in fp32 --------------
 

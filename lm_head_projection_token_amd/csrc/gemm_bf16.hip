@@ -9,7 +9,8 @@
 //   dX      dX = dZ W                  A = dZ   [C x V]   K-contiguous
 //                                      B = W    (K = V)   N-contiguous
 //   dW      dW (+)= dZ^T X             A = dZ^T (K = C)   M-contiguous
-//                                      B = X    (K = C)   N-contiguous
+//                                      B = X^T  (K = C)   K-contiguous (the chunk's
+//                                                         X transposed once)
 //
 // One kernel template serves all three. A workgroup of 256 threads (four
 // wavefronts in a 2 x 2 grid) computes a 256 x 256 tile; each wavefront owns
@@ -108,6 +109,7 @@ static_assert(4 * kSlabBytes + BN * 4 + BM * 4 <= NSTAGE * kStageBytes,
 constexpr unsigned kOOB = 0x80000000u;          // offset outside every descriptor
 constexpr unsigned kMaxRecords = 0x7fffffffu;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;                 // cache policy of a buffer load: nt
 
 // Swizzles of the 16-byte chunk index. K-contiguous tiles (4 chunks per row):
 // the 16 rows that 16 lanes of one ds_read_b128 touch spread over all banks.
@@ -336,7 +338,8 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
 template <bool B16>
 struct EpiLogits {
   static constexpr bool kRowStats = true;
-  static constexpr bool kReadModifyWrite = false;
+  static constexpr bool kSeedAcc = false;
+  static constexpr bool kColSums = false;
   void *S;
   int64_t lds;
   const unsigned short *bias;
@@ -396,7 +399,8 @@ struct EpiLogits {
 // Stores four consecutive columns n .. n + 3 of row m (n is a multiple of 4).
 struct EpiDx {
   static constexpr bool kRowStats = false;
-  static constexpr bool kReadModifyWrite = false;
+  static constexpr bool kSeedAcc = false;
+  static constexpr bool kColSums = false;
   unsigned short *out;
   int64_t ldo;
   float *partial;
@@ -439,15 +443,24 @@ struct EpiDx {
   }
 };
 
-// dW epilogue: fp32 store, or read-modify-write across token chunks (each
-// tile owns its rows, so there are no atomics). The interior tiles' loads and
-// stores are non-temporal: dW (GBs) is touched once per chunk.
+// dW: fp32, accumulated across token chunks (each tile owns its rows, so
+// there are no atomics). On every chunk after the first the accumulators
+// start from the tile's old values, loaded together with the first operand
+// slices, so the epilogue only stores: the fp32 read overlaps the start of
+// the K loop instead of following it. The interior tiles' loads and stores
+// are non-temporal: dW (GBs) is touched once per chunk.
+// db (when given) is formed in the same tiles: the tiles of N-block 0 also
+// sum their dZ^T rows over the chunk's tokens, with MFMAs against a
+// fragment of ones [frozen lm_head GRPO page, Summary: the bias gradient
+// with the weight's, only when asked for].
 struct EpiDw {
   static constexpr bool kRowStats = false;
-  static constexpr bool kReadModifyWrite = true;
+  static constexpr bool kSeedAcc = true;
+  static constexpr bool kColSums = true;
   float *dW;
   int64_t ld;
   int accumulate;
+  float *db;  // [M] fp32, or null
   __device__ __forceinline__ f32x4 load4_in(int64_t m, int64_t n) const {
     if (!accumulate) return f32x4{0.f, 0.f, 0.f, 0.f};
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(dW + m * ld + n));
@@ -488,6 +501,7 @@ struct EpiDw {
 __device__ __forceinline__ void mfma(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
 // max of three floats (v_max3_f32). fmaxf on values read from accumulator
 // registers would first quiet each input with an extra v_max_f32 copy.
 __device__ __forceinline__ float max3(float a, float b, float c) {
@@ -573,9 +587,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const unsigned lds_base = unsigned(reinterpret_cast<uintptr_t>(lds));
 
   // K-contiguous operands load pairs of slices, MN-contiguous ones single
-  // slices: both paired (logits), A paired and B single (dX), both single (dW).
+  // slices: both paired (logits), one paired and the other single (dX: A
+  // paired; dW over the transposed X: B paired), both single otherwise.
   constexpr bool PAIRED = A_K && B_K;
-  constexpr bool HYBRID = A_K && !B_K;
+  constexpr bool HYBRID = A_K != B_K;
   using OA = typename std::conditional<A_K, OpK, OpMN>::type;
   using OB = typename std::conditional<B_K, OpK, OpMN>::type;
   OA opa;
@@ -586,13 +601,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     opb.init(d.B, d.ldb, n0, d.N, kbeg, wave, lane, wn * 128, lds_base + kOperandBytes);
   else opb.init(d.B, d.ldb, n0, wave, lane, wn * 128, lds_base + kOperandBytes);
   LDS_AS char *lds_a = lds, *lds_b = lds + kOperandBytes;
+  // hybrid: the paired (K-contiguous) operand and the single one, with their
+  // LDS bases
+  auto &opP = [&]() -> auto & {
+    if constexpr (B_K && !A_K) return opb;
+    else return opa;
+  }();
+  auto &opS = [&]() -> auto & {
+    if constexpr (B_K && !A_K) return opa;
+    else return opb;
+  }();
+  LDS_AS char *lds_P = (B_K && !A_K) ? lds_b : lds_a;
+  LDS_AS char *lds_S = (B_K && !A_K) ? lds_a : lds_b;
 
   // acc[i][j]: the 16 x 16 block of rows wm * 128 + 16 i, columns wn * 128 + 16 j
   f32x4 acc[8][8];
+  const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
+  // every column of this wave is below N / every row and column is inside
+  const bool full = nw + 128 <= d.N;
+  const bool interior = full && mw + 128 <= d.M;
+  if constexpr (Epi::kSeedAcc) {
+    // The tile's old values, in the accumulator layout (lane l: row
+    // 16 i + l % 16, columns 16 j + 4 (l / 16) .. + 3), loaded straight into
+    // the accumulators before the operand slices, so the prologue's wait
+    // covers them. One descriptor per tile: rows past M lie outside its
+    // range and read as zero, and so does everything on the first chunk
+    // (range 0: no branch, the loads return zeros without a memory access);
+    // a column group past N (N is a multiple of 4) is pointed outside it.
+    const int64_t rows_left = d.M - m0;
+    const int64_t range =
+        epi.accumulate ? (rows_left < BM ? rows_left : BM) * epi.ld * 4 : int64_t(0);
+    const __amdgpu_buffer_rsrc_t r = rsrc(epi.dW + m0 * epi.ld, range);
+    // element (m, n) lies (m - m0) * ld + n floats past the descriptor's base
+    const unsigned lane_off =
+        unsigned(((wm * 128 + (lane & 15)) * epi.ld + nw + 4 * (lane >> 4)) * 4);
+    const int64_t nc = nw + 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const unsigned vi = lane_off + unsigned(i * 16 * epi.ld * 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < 8; ++j) {
+        const unsigned v = full || nc + 16 * j < d.N ? vi + 64u * j : kOOB;
+        acc[i][j] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v, 0, kNonTemporal));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // db: the wave holding the first 128 columns of N-block 0 sums its 128
+  // rows of A over K: each lane adds the eight K-values of its fragments
+  // with v_dot2 against ones, the four K-groups are merged at the end
+  bool col_sums = false;
+  if constexpr (Epi::kColSums) col_sums = epi.db != nullptr && tn == 0 && wn == 0;
+  float csum[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) csum[i] = 0.0f;
 
   // K-step kt (the last one may be partial) multiplies the fragments of
   // slice kt, held in registers; meanwhile it reads the fragments of slice
@@ -623,8 +690,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
       }
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
     } else if constexpr (HYBRID) {
-      // in the order the steady state issues them: B 0, B 1, A (0, 1),
-      // B 2, B 3, A (2, 3); slice 0 of both needs all but the last 16
+      // in the order the steady state issues them: single 0, single 1,
+      // pair (0, 1), single 2, single 3, pair (2, 3); slice 0 of both needs
+      // all but the last 16
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
@@ -632,11 +700,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
           const int sl = 2 * pr + t;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            opb.template issue_one<true>(lds_b, sl, wave, q, kbeg + int64_t(sl) * BK, kend);
+            opS.template issue_one<true>(lds_S, sl, wave, q, kbeg + int64_t(sl) * BK, kend);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          opa.template issue_pair<true>(lds_a, 2 * pr, wave, q, kbeg + int64_t(2 * pr) * BK, kend);
+          opP.template issue_pair<true>(lds_P, 2 * pr, wave, q, kbeg + int64_t(2 * pr) * BK, kend);
       }
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
     } else {
@@ -680,10 +748,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     // paired, those of the pair after the one holding slice kt + 1 (none at
     // odd steps, whose slice kt + 1 starts the most recently loaded pair);
     // single, those of slices kt + 2 and kt + 3.
-    // hybrid: at even steps B's slices kt + 2, kt + 3 and A's pair after the
-    // one holding slice kt + 1 (16); at odd steps only the B slice loaded
-    // by the step before (4), since A's pair holding slice kt + 1 was the
-    // last thing issued before it.
+    // hybrid: at even steps the single operand's slices kt + 2, kt + 3 and
+    // the paired operand's pair after the one holding slice kt + 1 (16); at
+    // odd steps only the single slice loaded by the step before (4), since
+    // the pair holding slice kt + 1 was the last thing issued before it.
     constexpr int vm = PAIRED   ? (load_pair ? 0 : kLoadsPerPair)
                        : HYBRID ? ((u & 1) ? 4 : kLoadsPerPair)
                                 : kVmcntLoop;
@@ -707,14 +775,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
           opb.template issue_pair<CHECK>(lds_b, slot_load, wave, q - 8, k_load, kend);
       }
       if constexpr (HYBRID && (u & 1) && (x & 3) == 2) {
-        constexpr int q = x >> 2;  // B's 4 loads first, then A's 8 pair loads
+        constexpr int q = x >> 2;  // the single slice's 4 loads, then the pair's 8
         if constexpr (q < 4)
-          opb.template issue_one<CHECK>(lds_b, slot_load, wave, q, k_load, kend);
+          opS.template issue_one<CHECK>(lds_S, slot_load, wave, q, k_load, kend);
         else if constexpr (q < 12)
-          opa.template issue_pair<CHECK>(lds_a, slot_pair, wave, q - 4, k_pair, kend);
+          opP.template issue_pair<CHECK>(lds_P, slot_pair, wave, q - 4, k_pair, kend);
       }
       if constexpr (HYBRID && !(u & 1) && (x & 15) == 4)
-        opb.template issue_one<CHECK>(lds_b, slot_load, wave, x >> 4, k_load, kend);
+        opS.template issue_one<CHECK>(lds_S, slot_load, wave, x >> 4, k_load, kend);
       if constexpr (!PAIRED && !HYBRID && (x & 7) == 4) {
         constexpr int q = x >> 3;
         if constexpr (q < 4)
@@ -723,6 +791,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
           opb.template issue_one<CHECK>(lds_b, slot_load, wave, q - 4, k_load, kend);
       }
     });
+    if constexpr (Epi::kColSums) {
+      if (col_sums) {
+        // the four bf16 pairs of each fragment, taken with shuffles: an
+        // element of a bit-cast vector passed to the builtin compiled to the
+        // first pair four times
+        const bf16x2_t one2 = {1.0, 1.0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 f = fa[cur][i];
+          float c = csum[i];
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one2, c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one2, c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one2, c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one2, c, false);
+          csum[i] = c;
+        }
+      }
+    }
   };
 
   // Full-speed steps: the slice each one loads lies wholly before kend.
@@ -774,36 +860,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
   const int lcol = 4 * (lane >> 4);
   const int crow = lane >> 5;        // coalesced layout: row 2 j + crow of the slab,
   const int ccol = 4 * (lane & 31);  // columns ccol .. ccol + 3 of the wave's 128
-  const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
-
-  // every column of this wave is below N / every row and column is inside
-  const bool full = nw + 128 <= d.N;
-  const bool interior = full && mw + 128 <= d.M;
   constexpr float kLog2e = 1.4426950408889634f;
 
-  // dW: the old values of slabs i and i + 1 are in flight while slab i is
-  // transposed and stored.
-  f32x4 old[2][8];
-  auto load_old = [&](int i, f32x4(&o)[8]) __attribute__((always_inline)) {
-    if constexpr (Epi::kReadModifyWrite) {
-      int64_t mrow = mw + i * 16 + crow;
-      asm volatile("" : "+v"(mrow));
-      if (interior) {
+  // db: the chunk's column sums, added to what earlier chunks left (each row
+  // of db belongs to one tile: no atomics)
+  if constexpr (Epi::kColSums) {
+    if (col_sums) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = epi.load4_in(mrow + 2 * j, nw + ccol);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float4 t = mrow + 2 * j < d.M ? epi.load4(mrow + 2 * j, nw + ccol, d.N)
-                                              : make_float4(0.f, 0.f, 0.f, 0.f);
-          o[j] = f32x4{t.x, t.y, t.z, t.w};
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float t = quad_sum(csum[i]);  // lanes q, q + 16, q + 32, q + 48
+        const int64_t m = mw + 16 * i + lane;
+        if (lane < 16 && m < d.M) epi.db[m] = epi.accumulate ? epi.db[m] + t : t;
       }
     }
-  };
-  if constexpr (Epi::kReadModifyWrite) {
-    load_old(0, old[0]);
-    load_old(1, old[1]);
   }
 
   // One 16-row slab; I is a compile-time constant so that acc[I] stays in
@@ -899,15 +968,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       rd[j] = *(const LDS_AS f32x4 *)(slab + (2 * j + crow) * kSlabPitch + ccol);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if constexpr (Epi::kReadModifyWrite) {
-        rd[j].x += old[i & 1][j].x;
-        rd[j].y += old[i & 1][j].y;
-        rd[j].z += old[i & 1][j].z;
-        rd[j].w += old[i & 1][j].w;
-      }
-    }
     int64_t mrow = mw + i * 16 + crow;
     asm volatile("" : "+v"(mrow));  // row addresses are formed here, per slab
     if (interior) {
@@ -919,9 +979,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
         if (mrow + 2 * j < d.M)
           epi.store4(mrow + 2 * j, nw + ccol, d.N,
                      make_float4(rd[j].x, rd[j].y, rd[j].z, rd[j].w), split);
-    }
-    if constexpr (Epi::kReadModifyWrite) {
-      if constexpr (i + 2 < 8) load_old(i + 2, old[i & 1]);
     }
   };
   static_for<8>([&](auto I) __attribute__((always_inline)) { do_slab(I); });
@@ -992,13 +1049,14 @@ void launch_dx_bf16(const void *dZ, int64_t ldz, const void *W, int64_t ldw, voi
   launch<true, false>(d, e, st);
 }
 
-void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx, float *dW,
-                    int64_t M, int64_t N, int64_t K, int accumulate, hipStream_t st) {
+void launch_dw_bf16(const void *dZ, int64_t ldz, const void *XT, int64_t ldxt, float *dW,
+                    float *db, int64_t M, int64_t N, int64_t K, int accumulate,
+                    hipStream_t st) {
   GemmDesc d{};
   d.A = static_cast<const unsigned short *>(dZ);
   d.lda = ldz;
-  d.B = static_cast<const unsigned short *>(X);
-  d.ldb = ldx;
+  d.B = static_cast<const unsigned short *>(XT);
+  d.ldb = ldxt;
   d.M = M;
   d.N = N;
   d.K = K;
@@ -1007,8 +1065,8 @@ void launch_dw_bf16(const void *dZ, int64_t ldz, const void *X, int64_t ldx, flo
   d.group = 4;
   d.n_first = 1;
   d.xcd_remap = 1;
-  EpiDw e{dW, N, accumulate};
-  launch<false, false>(d, e, st);
+  EpiDw e{dW, N, accumulate, db};
+  launch<false, true>(d, e, st);
 }
 
 }  // namespace fll

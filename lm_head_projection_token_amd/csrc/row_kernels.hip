@@ -742,6 +742,29 @@ __global__ void dx_reduce_kernel(const float *P, int64_t splits, int64_t M, int6
   }
 }
 
+// bf16 transpose through LDS: a 64 x 64 tile per 256-thread workgroup,
+// read and written along rows (each thread four elements of a row per
+// pass); the LDS row pitch of 65 halfwords keeps the column reads spread
+// over the banks.
+constexpr int kTr = 64;
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const unsigned short *X,
+                                                             int64_t ldx, int64_t rows,
+                                                             int64_t cols, unsigned short *XT,
+                                                             int64_t ldt) {
+  __shared__ unsigned short tile[kTr][kTr + 1];
+  const int64_t r0 = int64_t(blockIdx.y) * kTr, c0 = int64_t(blockIdx.x) * kTr;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
+  for (int i = ty; i < kTr; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? X[r * ldx + c] : (unsigned short)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < kTr; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) XT[c * ldt + r] = tile[tx][i];
+  }
+}
+
 __global__ void fill_kernel(float *p, int64_t n, float v) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * blockDim.x)
@@ -805,6 +828,15 @@ void launch_finalize(const float *rowval, const float *weights, int64_t BT,
                      const DevScalars *sc, float *loss, hipStream_t st) {
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, rowval, weights, BT, sc,
                      loss);
+}
+
+void launch_transpose_bf16(const void *X, int64_t ldx, int64_t rows, int64_t cols, void *XT,
+                           int64_t ldt, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return;
+  const dim3 grid(unsigned((cols + kTr - 1) / kTr), unsigned((rows + kTr - 1) / kTr));
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, st,
+                     static_cast<const unsigned short *>(X), ldx, rows, cols,
+                     static_cast<unsigned short *>(XT), ldt);
 }
 
 void launch_fill(float *p, int64_t n, float v, hipStream_t st) {

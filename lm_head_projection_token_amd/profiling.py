@@ -43,6 +43,7 @@ KINDS = [
     ("gemm_f32_kernel", "gemm_fp32"), ("row_kernel", "row"),
     ("dx_reduce_kernel", "dx_reduce"), ("colsum_kernel", "db"),
     ("finalize_kernel", "final"), ("prep_kernel", "prep"), ("fill_kernel", "fill"),
+    ("transpose_bf16_kernel", "transpose"),
 ]
 
 

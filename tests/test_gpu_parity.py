@@ -76,6 +76,11 @@ SMALL = {
         BT=130, H=72, V=333, dtype="fp32", head="ppo", has_bias=True, compute_dW=True,
         compute_db=True, clip_low=0.1, clip_high=0.1, logratio_std=0.3, x_std=1.0,
         w_std=0.1, seed=43),
+    # db with a frozen weight (the column-sum kernel; with dW, db is formed
+    # inside the dW GEMM), a vocabulary tail in the last 256-row tile
+    "sel-bf16-db-only-frozen-weight": workloads.small_case(
+        BT=520, H=136, V=1100, dtype="bf16", head="selective", has_bias=True,
+        compute_db=True, reduction="sum", ignore_frac=0.05, w_std=0.05, seed=46),
     "ppo-bf16-no-clip-two-vocab-chunks": workloads.small_case(
         BT=257, H=64, V=4099, dtype="bf16", head="ppo", clip_low=1.0,
         clip_high=float("inf"), logratio_std=0.5, reduction="mean", w_std=0.05, seed=44),
