@@ -48,7 +48,8 @@ void launch_dw_bf16(const void *dZ, int64_t ldz, const void *XT, int64_t ldxt,
                     float *dW, float *db, int64_t M, int64_t N, int64_t K,
                     int accumulate, hipStream_t st);
 
-// XT[c, r] = X[r, c] for r < rows, c < cols (bf16): X pitch ldx, XT pitch ldt.
+// XT[c, r] = X[r, c] for r < rows, c < cols (bf16): X pitch ldx, XT pitch
+// ldt >= rows rounded up to 8; XT[c, r] = 0 for rows <= r < that multiple.
 void launch_transpose_bf16(const void *X, int64_t ldx, int64_t rows, int64_t cols, void *XT,
                            int64_t ldt, hipStream_t st);
 

@@ -745,13 +745,17 @@ __global__ void dx_reduce_kernel(const float *P, int64_t splits, int64_t M, int6
 // bf16 transpose through LDS: a 64 x 64 tile per 256-thread workgroup,
 // read and written along rows (each thread four elements of a row per
 // pass); the LDS row pitch of 65 halfwords keeps the column reads spread
-// over the banks.
+// over the banks. XT's columns from `rows` to the next multiple of 8 are
+// written as zeros: the GEMM reads K in groups of 8, and a group that
+// straddles the end must add nothing (the bytes there may hold anything,
+// e.g. the dX partial sums that share the buffer).
 constexpr int kTr = 64;
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const unsigned short *X,
                                                              int64_t ldx, int64_t rows,
                                                              int64_t cols, unsigned short *XT,
                                                              int64_t ldt) {
   __shared__ unsigned short tile[kTr][kTr + 1];
+  const int64_t rows8 = (rows + 7) & ~int64_t(7);
   const int64_t r0 = int64_t(blockIdx.y) * kTr, c0 = int64_t(blockIdx.x) * kTr;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
   for (int i = ty; i < kTr; i += 4) {
@@ -761,7 +765,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const unsigned shor
   __syncthreads();
   for (int i = ty; i < kTr; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) XT[c * ldt + r] = tile[tx][i];
+    if (c < cols && r < rows8) XT[c * ldt + r] = tile[tx][i];
   }
 }
 
@@ -833,7 +837,8 @@ void launch_finalize(const float *rowval, const float *weights, int64_t BT,
 void launch_transpose_bf16(const void *X, int64_t ldx, int64_t rows, int64_t cols, void *XT,
                            int64_t ldt, hipStream_t st) {
   if (rows <= 0 || cols <= 0) return;
-  const dim3 grid(unsigned((cols + kTr - 1) / kTr), unsigned((rows + kTr - 1) / kTr));
+  const int64_t rows8 = (rows + 7) & ~int64_t(7);  // ldt >= rows8
+  const dim3 grid(unsigned((cols + kTr - 1) / kTr), unsigned((rows8 + kTr - 1) / kTr));
   hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, st,
                      static_cast<const unsigned short *>(X), ldx, rows, cols,
                      static_cast<unsigned short *>(XT), ldt);

@@ -42,7 +42,12 @@ def test_cfg2_full():
 # V=128256 GRPO workload, with a trainable head (beyond the five workloads).
 CE_FULL = workloads.WORKLOADS[3].replace(name="ce-bf16-trainable-B8T1024-V128256", head="ce",
                                          compute_dW=True, ignore_frac=0.05, seed=6)
-EXTRA = {"ce": CE_FULL, "jsd": workloads.JSD_WORKLOAD}
+# The PPO clipped surrogate (the GRPO family) at the same shape, with a
+# trainable head and ignored rows; its old log-probs are the oracle's
+# log p(y) minus drawn log-ratios kept off the clip edges.
+PPO_FULL = workloads.PPO_WORKLOAD.replace(name="ppo-bf16-trainable-B8T1024-V128256",
+                                          compute_dW=True, ignore_frac=0.05)
+EXTRA = {"ce": CE_FULL, "jsd": workloads.JSD_WORKLOAD, "ppo": PPO_FULL}
 
 # which workloads are also run with bf16 chunk logits against the same oracle
 BF16_LOGITS_TOO = {3, 5, "jsd"}
@@ -73,7 +78,7 @@ def _compare(out, ref, case, inp, logits_bf16):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", [3, 4, 5, "ce", "jsd"])
+@pytest.mark.parametrize("cfg", [3, 4, 5, "ce", "jsd", "ppo"])
 def test_full_config(cfg):
     case = EXTRA[cfg] if cfg in EXTRA else workloads.WORKLOADS[cfg]
     print(f"[cfg{cfg}] {case}", flush=True)

@@ -81,6 +81,13 @@ SMALL = {
     "sel-bf16-db-only-frozen-weight": workloads.small_case(
         BT=520, H=136, V=1100, dtype="bf16", head="selective", has_bias=True,
         compute_db=True, reduction="sum", ignore_frac=0.05, w_std=0.05, seed=46),
+    # a ragged last chunk (44 tokens) with the dX vocabulary split (4
+    # splits), a trainable head and bias: the transposed X of the dW GEMM
+    # shares its buffer with the dX partial sums
+    "sel-bf16-ragged-chunk-split-dx-trainable": workloads.small_case(
+        BT=300, H=136, V=8192, dtype="bf16", head="selective", has_bias=True,
+        compute_dW=True, compute_db=True, reduction="mean", ignore_frac=0.05,
+        w_std=0.05, seed=47),
     "ppo-bf16-no-clip-two-vocab-chunks": workloads.small_case(
         BT=257, H=64, V=4099, dtype="bf16", head="ppo", clip_low=1.0,
         clip_high=float("inf"), logratio_std=0.5, reduction="mean", w_std=0.05, seed=44),
