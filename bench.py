@@ -366,11 +366,14 @@ def main():
     dom = max(gemms, key=lambda k: kernels[k]["ms_per_step"])
     per_launch = kernel_flops(dom, case) / plan.n_chunks
     achieved = per_launch / (kernels[dom]["avg_ms"] / 1e3) / 1e12
+    # the teacher's logits GEMM is the logits kernel: the counter summaries
+    # (by kernel) hold it under that name, averaged with the student's
+    prof_kind = "logits" if dom == "teacher" else dom
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": measured_traffic(case, dom, args.logits_bf16),
+                "traffic": measured_traffic(case, prof_kind, args.logits_bf16),
                 "flops_per_launch": per_launch}
-    clk = measured_clock(case, dom, args.logits_bf16)
+    clk = measured_clock(case, prof_kind, args.logits_bf16)
     if clk:
         # the clock this kernel ran at, from the committed counter summary
         # (GRBM_COUNT over the kernel's duration) of the same kernel sources
