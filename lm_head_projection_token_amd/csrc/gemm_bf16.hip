@@ -761,12 +761,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
     // 64 MFMAs; between them the reads of slice kt + 1 and the loads: paired,
     // at odd steps, the 16 of the next pair (8 of A, then 8 of B); single, 8
     // per step (4 of A, then 4 of B).
-    constexpr int ea = 64 / OA::kReads, eb = 64 / OB::kReads;
+    // A's read r follows MFMA ea * r, B's read r MFMA eb / 2 + eb * r. The
+    // spacing was measured per product: the logits GEMM spreads its reads
+    // over the whole step (closer spacings ran it 1-2 % slower); dX issues
+    // its 16 transpose reads of W every second MFMA, done by mid-step so
+    // their latency is covered before the next step's wait (dX 3.3 %
+    // faster than one every fourth); dW its 8 reads of the transposed X
+    // every sixth (about 1 %).
+    constexpr int ea = 64 / OA::kReads;
+    constexpr int eb = (A_K && !B_K) ? 2 : (!A_K && B_K) ? 6 : 64 / OB::kReads;
+    static_assert(ea * (OA::kReads - 1) < 64 && eb / 2 + eb * (OB::kReads - 1) < 64,
+                  "every read of slice kt + 1 is issued inside the step");
     static_for<64>([&](auto X_) __attribute__((always_inline)) {
       constexpr int x = decltype(X_)::value;
       mfma(acc[x >> 3][x & 7], fb[cur][x & 7], fa[cur][x >> 3]);
       if constexpr (x % ea == 0) opa.template read<slot_nxt, x / ea>(fa[nxt]);
-      if constexpr (x % eb == eb / 2) opb.template read<slot_nxt, x / eb>(fb[nxt]);
+      if constexpr (x >= eb / 2 && (x - eb / 2) % eb == 0 && (x - eb / 2) / eb < OB::kReads)
+        opb.template read<slot_nxt, (x - eb / 2) / eb>(fb[nxt]);
       if constexpr (load_pair && (x & 3) == 2) {
         constexpr int q = x >> 2;
         if constexpr (q < 8)
