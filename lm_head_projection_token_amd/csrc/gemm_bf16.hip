@@ -936,8 +936,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
               if (nw + 16 * j + lcol + e < d.N) mx = fmaxf(mx, v[j][e]);
         }
         mx = quad_max(mx);
-        // exp(v - mx) = 2^(v log2(e) - mx log2(e))
-        const float off = mx == -INFINITY ? 0.0f : -mx * kLog2e;
+        // exp(v - mx) = 2^((v - mx) log2(e)), the difference taken first so
+        // the maximum itself adds exactly 1 (with v log2(e) - mx log2(e) as
+        // one fma, the rounding of mx log2(e) left a one-entry vocabulary a
+        // log-sum-exp an ulp off its logit, and exact zeros became 1e-7)
+        const float mxs = mx == -INFINITY ? 0.0f : mx;
         float se = 0.0f;
         if (full) {
           // four independent sums (one per element of the 4-column group)
@@ -945,7 +948,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
           for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s4[e] += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
+            for (int e = 0; e < 4; ++e) s4[e] += __builtin_amdgcn_exp2f((v[j][e] - mxs) * kLog2e);
           se = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         } else if (mx != -INFINITY) {
 #pragma unroll
@@ -953,7 +956,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmDesc d, Epi epi) 
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (nw + 16 * j + lcol + e < d.N)
-                se += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, off));
+                se += __builtin_amdgcn_exp2f((v[j][e] - mxs) * kLog2e);
         }
         se = quad_sum(se);
         if (lane < 16 && m < d.M && nw < d.N)
