@@ -389,7 +389,8 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
 
     Returns a dict with loss (float), per_row [BT] (KL_r, log p(y_r),
     -log p(y_r), JS_r or the ratio heads' L_r; 0 on ignored rows), dX [BT, H],
-    dW [V, H] or None, db [V] or None, n_valid, g. The JSD head takes the
+    dW [V, H] or None, db [V] or None, n_valid, g, and dZ [BT, V], the
+    gradient with respect to the raw logits (dX = dZ W, dW = dZ^T X). The JSD head takes the
     teacher's X_teacher [BT, H_t], W_teacher [V, H_t] (+ b_teacher [V]) and no
     ``target``; the ratio heads take ``old_logprobs`` [BT] and the advantages
     as ``weights``.
@@ -407,7 +408,7 @@ def fwd_bwd(X, W, b=None, *, head, labels=None, target=None, weights=None,
                      X_teacher=X_teacher, W_teacher=W_teacher, b_teacher=b_teacher,
                      old_logprobs=old_logprobs, clip_low=clip_low, clip_high=clip_high)
     loss = g * float((w * L).sum())
-    out = dict(loss=loss, per_row=L, n_valid=n_valid, g=g, dW=None, db=None)
+    out = dict(loss=loss, per_row=L, n_valid=n_valid, g=g, dW=None, db=None, dZ=dZ)
     out["dX"] = dZ @ W
     if compute_dW:
         out["dW"] = dZ.T @ X
