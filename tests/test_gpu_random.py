@@ -64,10 +64,31 @@ def draw(i):
     return case, chunk, logits_bf16
 
 
+N_MEDIUM = 6
+
+
+def draw_medium(i):
+    """Medium case i: bf16, a few thousand tokens and tens of thousands of
+    vocabulary entries, so the dX GEMM splits the vocabulary and the batch
+    spans several chunks, with the other options drawn as in ``draw``."""
+    rng = np.random.default_rng(8000 + i)
+    small, chunk, lb = draw(100 + i)
+    BT = int(rng.choice([777, 1500, 2100]))
+    Hd = 8 * int(rng.integers(32, 129))
+    V = int(rng.choice([8191, 16384, 32000, 40000]))
+    kw = {}
+    if small.head == "jsd":
+        kw["H_teacher"] = 8 * int(rng.integers(16, 65))
+    case = small.replace(name=f"medium-{small.head}-{BT}x{Hd}x{V}", BT=BT, H=Hd, V=V,
+                         dtype="bf16", seed=8000 + i, **kw)
+    chunk = int(rng.integers(256, BT + 1)) if rng.random() < 0.3 else 0
+    return case, chunk, bool(rng.random() < 0.25)
+
+
 def test_random_cases_are_valid_plans():
     # host only: every drawn problem is accepted and planned as drawn
-    for i in range(N_CASES):
-        case, chunk, lb = draw(i)
+    drawn = [draw(i) for i in range(N_CASES)] + [draw_medium(i) for i in range(N_MEDIUM)]
+    for i, (case, chunk, lb) in enumerate(drawn):
         prob = fll.make_problem(
             case.BT, case.H, case.V, dtype=case.dtype, head=case.head,
             has_bias=case.has_bias, compute_dW=case.compute_dW,
@@ -83,11 +104,7 @@ def test_random_cases_are_valid_plans():
         assert plan.n_chunks * plan.chunk_rows >= case.BT, i
 
 
-@pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_case_parity(i):
-    case, chunk, lb = draw(i)
-    print(f"[random {i}] {case} chunk_rows={chunk} logits_bf16={lb}", flush=True)
+def _parity(case, chunk, lb):
     inp = H.make(case)
     extra = H.fp32_cancellation_floor(inp, case)
     if lb and case.head not in workloads.LABEL_HEADS:
@@ -96,6 +113,22 @@ def test_random_case_parity(i):
     if chunk:
         assert out["plan"].chunk_rows == chunk
     H.compare_full(out, H.run_oracle(inp, case), case, per_row_atol=extra, inp=inp)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case_parity(i):
+    case, chunk, lb = draw(i)
+    print(f"[random {i}] {case} chunk_rows={chunk} logits_bf16={lb}", flush=True)
+    _parity(case, chunk, lb)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_MEDIUM))
+def test_random_medium_case_parity(i):
+    case, chunk, lb = draw_medium(i)
+    print(f"[random medium {i}] {case} chunk_rows={chunk} logits_bf16={lb}", flush=True)
+    _parity(case, chunk, lb)
 
 
 @pytest.mark.parametrize("i", [4, 16, 30])
