@@ -46,7 +46,9 @@
  *  - Plain C types only. Device pointers point to memory on the current HIP
  *    device; host pointers are marked "host".
  *  - The caller owns every buffer (inputs, outputs, workspace). The library
- *    allocates no device memory and keeps no pointer after a call returns.
+ *    allocates no device memory and keeps no pointer after a call returns
+ *    (fll_fwd_bwd_static takes its workspace from a fixed device array the
+ *    library holds instead of the caller's).
  *  - All matrices are row-major and densely packed (row pitch = row length).
  *  - Status codes are fll_status values. Every argument is checked on the
  *    host before anything is enqueued, so an argument, support or workspace
