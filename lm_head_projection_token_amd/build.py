@@ -71,5 +71,26 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+CLIENT_DIR = os.path.join(os.path.dirname(PKG), "tests", "c_client")
+CLIENT = os.path.join(CLIENT_DIR, "fll_client")
+
+
+def build_c_client() -> str:
+    """Compile the plain C client of the library (``tests/c_client``) with
+    gcc against include/fll.h, the in-tree libfll.so and the HIP runtime; it
+    finds libfll.so next to the repository at run time (rpath $ORIGIN)."""
+    src = os.path.join(CLIENT_DIR, "fll_client.c")
+    tmp = CLIENT + ".tmp"
+    _run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror",
+          "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", os.path.join(ROCM, "include"),
+          src, "-o", tmp, "-L", PKG, "-lfll", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../../lm_head_projection_token_amd",
+          "-Wl,-rpath," + os.path.join(ROCM, "lib")])
+    os.replace(tmp, CLIENT)
+    return CLIENT
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_client()
