@@ -10,7 +10,9 @@
 * H = 2^20, the largest hidden size: a 32768-step K loop in the logits GEMM
   and 4096 output tiles across H in dX and dW. V is small, so the oracle
   runs in full.
-Both with a trainable head and a bias, in bf16 at the stated tolerances.
+* BT = 70001 tokens: the chunk size at its 8192-row cap, nine chunks with a
+  ragged last one, dW and db accumulated over all of them; oracle in full.
+All with a trainable head and a bias, in bf16 at the stated tolerances.
 """
 
 import numpy as np
@@ -74,3 +76,19 @@ def test_largest_hidden_size():
     inp = H.make(case)
     out = H.run_gpu(inp, case)
     H.compare_full(out, H.run_oracle(inp, case), case)
+
+
+@pytest.mark.parametrize("head", ["selective", "kl"])
+def test_many_chunks_at_the_chunk_cap(head):
+    # BT = 70001: the chunk size reaches its cap of 8192 rows, so the batch
+    # runs in 9 chunks, the last one ragged (4465 rows); dW and db are
+    # accumulated in fp32 over all of them. Oracle in full.
+    case = workloads.small_case(BT=70001, H=64, V=1000, dtype="bf16", head=head,
+                                has_bias=True, compute_dW=True, compute_db=True,
+                                reduction="mean", ignore_frac=0.05, w_std=0.05, seed=33)
+    print(f"[limits] BT = {case.BT}: {case}", flush=True)
+    inp = H.make(case)
+    out = H.run_gpu(inp, case)
+    plan = out["plan"]
+    assert plan.chunk_rows == 8192 and plan.n_chunks == 9
+    H.compare_full(out, H.run_oracle(inp, case), case, inp=inp)
