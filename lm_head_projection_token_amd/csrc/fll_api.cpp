@@ -335,7 +335,7 @@ int enqueue(const fll_plan_t *plan, const fll_args *args, hipStream_t s, bool ti
   int st = FLL_OK;
   // hipGetLastError reports the last failure of any HIP caller on this
   // thread; drop a stale one left by another library so only this call's
-  // launches are judged below.
+  // launches are checked below.
   (void)hipGetLastError();
   const fll_problem &p = plan->p;
   const fll_args &a = *args;

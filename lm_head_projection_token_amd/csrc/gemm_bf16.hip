@@ -35,7 +35,7 @@
 //   16-byte chunks XOR-swizzled by row, read with ds_read_b128. A pair is
 //   loaded during the odd K-step that frees its two slots, about one and a
 //   half K-steps before its first slice is read.
-//   MN-contiguous operands (B of dX, both of dW) load one slice per K-step,
+//   MN-contiguous operands (B of dX, A of dW) load one slice per K-step,
 //   four steps ahead (about two and a half K-steps before it is read): a
 //   shorter lead cost dX and dW 1-2 %, and their loads already cover whole
 //   lines.
