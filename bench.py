@@ -111,6 +111,31 @@ def kernel_flops(kind, case):
             "teacher": 2.0 * case.BT * case.H_teacher * case.V}.get(kind, 0.0)
 
 
+def gemm_bytes_per_launch(kind, case, n_chunks, logits_bf16=False):
+    """Algorithmic HBM bytes of one launch of a GEMM (a chunk of BT/n_chunks
+    rows on average): each operand read once and each output written once.
+    logits / teacher: X chunk, W (and b) read, the chunk's logits (4 or 2
+    bytes each) and its per-(row, 128-column) statistics written; dX: the
+    bf16 dZ chunk and W read, dX written; dW: the bf16 dZ chunk and the
+    chunk's X read, fp32 dW written, and read back on every chunk after the
+    first (averaged over the chunks)."""
+    es = 2 if case.dtype == "bf16" else 4
+    C = case.BT / max(n_chunks, 1)
+    V = case.V
+    nstat = -(-V // 128)
+    s = 2 if logits_bf16 else 4
+    if kind in ("logits", "teacher"):
+        Hk = case.H if kind == "logits" else case.H_teacher
+        bias = case.has_bias if kind == "logits" else case.teacher_has_bias
+        return C * Hk * es + V * Hk * es + (V * es if bias else 0) + C * V * s + C * nstat * 8
+    if kind == "dx":
+        return C * V * es + V * case.H * es + C * case.H * es
+    if kind == "dw":
+        old = (n_chunks - 1) / max(n_chunks, 1)
+        return C * V * es + C * case.H * es + V * case.H * 4 * (1 + old)
+    return 0.0
+
+
 def row_bytes_per_valid_row(case, logits_bf16=False):
     """Algorithmic HBM bytes of the row kernel per valid row: one read of the
     logits (and of the fp32 target or the teacher's logits) and one write of
@@ -372,7 +397,9 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic(case, prof_kind, args.logits_bf16),
-                "flops_per_launch": per_launch}
+                "flops_per_launch": per_launch,
+                "algorithmic_bytes_per_launch": gemm_bytes_per_launch(
+                    dom, case, plan.n_chunks, args.logits_bf16)}
     clk = measured_clock(case, prof_kind, args.logits_bf16)
     if clk:
         # the clock this kernel ran at, from the committed counter summary

@@ -43,6 +43,23 @@ def test_bench_flops_follow_the_gradient_flags():
     assert bench.gemm_flops(jsd) == 2.0 * jsd.BT * jsd.V * (2 * jsd.H + jsd.H_teacher)
 
 
+def test_bench_gemm_bytes_per_launch():
+    # each operand read once, each output written once, per launch of a
+    # 4096-row chunk (V = 128256, H = 4096, bf16)
+    c3 = workloads.WORKLOADS[3]
+    C, H, V = 4096, 4096, 128256
+    assert bench.gemm_bytes_per_launch("logits", c3, 2) == \
+        C * H * 2 + V * H * 2 + C * V * 4 + C * 1002 * 8
+    assert bench.gemm_bytes_per_launch("logits", c3, 2, logits_bf16=True) == \
+        C * H * 2 + V * H * 2 + C * V * 2 + C * 1002 * 8
+    assert bench.gemm_bytes_per_launch("dx", c3, 2) == C * V * 2 + V * H * 2 + C * H * 2
+    # dW of the two-chunk V = 151936 workload: fp32 dW written twice, read once
+    c4 = workloads.WORKLOADS[4]
+    V4 = 151936
+    assert bench.gemm_bytes_per_launch("dw", c4, 2) == \
+        C * V4 * 2 + C * H * 2 + V4 * H * 4 * 1.5
+
+
 def test_bench_row_bytes_per_valid_row():
     V = workloads.WORKLOADS[3].V
     # selective: read fp32 logits, write bf16 dlogits; KL also reads the fp32 target
