@@ -465,3 +465,69 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for k, v in outs.items():
             assert torch.equal(v, eager[k]), (rep, k)
+
+
+def test_concurrent_calls_on_two_streams_and_threads():
+    # the library keeps no state between calls: two problems, each with its
+    # own workspace, enqueued on two streams from two host threads at once,
+    # give bitwise the results each gives alone
+    import threading
+
+    import lm_head_projection_token_amd as fll
+
+    cases = [workloads.small_case(BT=520, H=136, V=1100, dtype="bf16", head="selective",
+                                  has_bias=True, compute_dW=True, compute_db=True,
+                                  reduction="mean", ignore_frac=0.05, w_std=0.05, seed=71),
+             workloads.small_case(BT=300, H=264, V=1000, dtype="bf16", head="kl",
+                                  compute_dW=True, temperature=2.0, ignore_frac=0.1,
+                                  w_std=0.05, seed=72)]
+    dev = "cuda:0"
+    runs = []
+    for case in cases:
+        inp = H.make(case)
+        d = {k: (None if inp.get(k) is None else inp[k].to(dev))
+             for k in ("X", "W", "b", "labels", "target", "weights")}
+        prob = fll.make_problem(case.BT, case.H, case.V, dtype="bf16", head=case.head,
+                                has_bias=case.has_bias, compute_dW=case.compute_dW,
+                                compute_db=case.compute_db, reduction=case.reduction,
+                                temperature=case.temperature)
+        plan = fll.fll_plan(prob)
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        outs = dict(dX=torch.empty_like(d["X"]), loss=torch.empty((), device=dev),
+                    dW=torch.empty(case.V, case.H, device=dev),
+                    db=torch.empty(case.V, device=dev) if case.compute_db else None)
+        runs.append((plan, d, ws, outs))
+
+    def call(run, stream=None):
+        plan, d, ws, outs = run
+        fll.fll_fwd_bwd(plan, **d, workspace=ws, stream=stream, **outs)
+
+    alone = []
+    for run in runs:
+        call(run)
+        torch.cuda.synchronize()
+        alone.append({k: v.clone() for k, v in run[3].items() if v is not None})
+        for v in run[3].values():
+            if v is not None:
+                v.fill_(float("nan"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    errors = []
+
+    def worker(i):
+        try:
+            for _ in range(3):
+                call(runs[i], streams[i])
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for run, ref in zip(runs, alone):
+        for k, v in ref.items():
+            assert torch.equal(run[3][k], v), k
