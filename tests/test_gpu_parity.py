@@ -202,18 +202,23 @@ def test_unnormalised_target():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_all_rows_ignored(dtype):
-    case = workloads.small_case(BT=64, H=32, V=100, dtype=dtype, head="selective",
-                                has_bias=True, compute_dW=True, compute_db=True, seed=22)
+@pytest.mark.parametrize("head", ["selective", "kl", "ce", "jsd", "ppo", "cispo"])
+def test_all_rows_ignored(dtype, head):
+    extra = dict(H_teacher=24) if head == "jsd" else {}
+    case = workloads.small_case(BT=64, H=32, V=100, dtype=dtype, head=head,
+                                has_bias=True, compute_dW=True, compute_db=True, seed=22,
+                                **extra)
     inp = H.make(case)
     inp["labels"][:] = case.ignore_index
+    if inp["target"] is not None:
+        inp["target"][:] = float("nan")  # ignored rows' targets are never read
     out = H.run_gpu(inp, case)
     assert float(out["loss"]) == 0.0
     for k in ("dX", "dW", "db", "per_row"):
         assert torch.count_nonzero(out[k]).item() == 0, k
 
 
-@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd", "ce", "ppo", "cispo"])
 def test_empty_batch(head):
     import lm_head_projection_token_amd as fll
 
@@ -227,6 +232,8 @@ def test_empty_batch(head):
     if head == "jsd":
         kw["X_teacher"] = torch.empty(0, 32, dtype=torch.bfloat16, device=dev)
         kw["W_teacher"] = torch.randn(50, 32, device=dev).to(torch.bfloat16)
+    if head in ("ppo", "cispo"):
+        kw["old_logprobs"] = torch.empty(0, device=dev)
     out = fll.fused_lm_head_loss(X, W, b, head=head, compute_dW=True, compute_db=True, **kw)
     torch.cuda.synchronize()
     assert float(out["loss"]) == 0.0
@@ -235,9 +242,12 @@ def test_empty_batch(head):
     assert torch.count_nonzero(out["db"]).item() == 0
 
 
-@pytest.mark.parametrize("head", ["kl", "selective", "jsd"])
+@pytest.mark.parametrize("head", ["kl", "selective", "jsd", "ce", "ppo", "cispo"])
 def test_single_token_vocabulary(head):
-    # V = 1: log p = 0 for every row, so the loss and every gradient vanish.
+    # V = 1: log p = 0 for every row, so every gradient vanishes exactly (the
+    # block statistics give the row maximum exactly 1, so p = 1); the loss
+    # is 0 too, except for the ratio heads, whose terms depend on the old
+    # log-probs and advantages only.
     extra = dict(H_teacher=24) if head == "jsd" else {}
     case = workloads.small_case(BT=40, H=16, V=1, dtype="bf16", head=head,
                                 compute_dW=True, seed=23, **extra)
