@@ -258,10 +258,13 @@ def test_single_token_vocabulary(head):
     assert torch.count_nonzero(out["dX"]).item() == 0
 
 
-def test_out_of_range_label_is_nan_not_a_fault():
-    case = workloads.small_case(BT=64, H=32, V=100, dtype="bf16", head="selective",
+@pytest.mark.parametrize("head", ["selective", "ce", "ppo", "cispo"])
+def test_out_of_range_label_is_nan_not_a_fault(head):
+    case = workloads.small_case(BT=64, H=32, V=100, dtype="bf16", head=head,
                                 compute_dW=True, seed=24)
     inp = H.make(case)
+    if head in workloads.RATIO_HEADS:
+        H.ratio_old_logprobs(inp, case)  # from the in-range labels
     inp["labels"][5] = 100   # == V
     inp["labels"][9] = -7    # negative, not ignore_index
     out = H.run_gpu(inp, case)
